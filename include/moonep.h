@@ -1,0 +1,213 @@
+/*
+ * moonep.h -- C ABI of a perfectly balanced expert-parallel MoE layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * R expert-parallel ranks are held as R partitions of one GPU's memory; the
+ * "symmetric memory" that lets every rank read every other rank's chunk is one
+ * device allocation, so no call here talks to another GPU.
+ *
+ * Sources, cited below by the short name in brackets:
+ *   [maestro]  ai-maestro.online, "Moonshot AI open-sources MoonEP, a perfectly
+ *              balanced expert parallelism library"
+ *   [spaxe]    spaxe.top, "Moonshot AI Open-Sources MoonEP: A Perfectly Balanced
+ *              Expert Parallelism Library for MoE Training" (paragraphs, 1-based)
+ *   [noticiai] noticiai.com.br, "Moonshot AI libera MoonEP: biblioteca de codigo
+ *              aberto para balanceamento perfeito em modelos MoE"
+ *
+ * Symbols: R ranks, S tokens per rank, E routed experts, G = E/R home experts
+ * per rank (rank p owns experts [pG, (p+1)G)), K experts per token, B prefetch
+ * slots per rank, H hidden size, Hp = H' the expert intermediate size,
+ * SK = S*K the fixed receive count of every rank, N = R*S tokens in all,
+ * g = r*S + s the global token id, u = g*K + k the flat (token, k) slot id.
+ *
+ * Conventions shared by every call:
+ *   - All arrays are caller-owned DEVICE memory, row-major, and must be 16-byte
+ *     aligned. The library allocates nothing and frees nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *     only enqueue work and return; none synchronises with the host or copies
+ *     device to host (except moonep_get_error), so the whole layer can be
+ *     captured in a HIP graph. Work is deterministic: no floating-point atomics.
+ *   - Arrays typed void* hold the layer dtype (bfloat16 or float32); gates and
+ *     every output of expert compute are float32.
+ *   - A call returns MOONEP_OK or a negative status before launching anything
+ *     when its arguments are invalid (see moonep_strerror).
+ *   - W_all is the [E+B,H,Hp] expert weight view of every rank at once: one
+ *     tensor of E + R*B rows [E+R*B, H, Hp]. Rank q's row i is W_all[i] for
+ *     i < E (the home experts, shared by all ranks) and W_all[E + q*B + (i-E)]
+ *     for i >= E (q's own prefetch slots) [maestro "The memory contract"].
+ */
+#ifndef MOONEP_H
+#define MOONEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moonep_shape {
+  int32_t R, S, E, K, B, H, Hp;
+  int32_t mode;   /* MOONEP_TRAIN or MOONEP_INFER */
+  int32_t dtype;  /* MOONEP_BF16 or MOONEP_FP32 */
+} moonep_shape;
+
+enum {
+  MOONEP_OK = 0,
+  MOONEP_EINVAL = -1,      /* bad shape, pointer, alignment or op */
+  MOONEP_EWORKSPACE = -2,  /* workspace smaller than moonep_workspace_bytes */
+  MOONEP_EHIP = -3,        /* a HIP runtime call or kernel launch failed */
+  MOONEP_EMODE = -4,       /* backward op requested on an inference layer */
+  MOONEP_ELIMIT = -5       /* shape beyond a documented size limit */
+};
+enum { MOONEP_TRAIN = 0, MOONEP_INFER = 1 };
+enum { MOONEP_BF16 = 0, MOONEP_FP32 = 1 };
+enum { MOONEP_FWD = 0, MOONEP_DGRAD = 1, MOONEP_WGRAD = 2 };
+/* bits of the sticky device error word read by moonep_get_error */
+enum { MOONEP_ERR_ID_RANGE = 1, MOONEP_ERR_ID_DUP = 2 };
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moonep_version(void);
+
+/* Human-readable text of a status code. Never NULL. */
+const char* moonep_strerror(int status);
+
+/*
+ * Validate a layer shape. Rules [maestro "The memory contract"; spaxe 7-8]:
+ *   E % R == 0; 0 <= B <= E/R; training needs B == E/R (replicas come from at
+ *   most one remote home group, so every touched expert is local); inference
+ *   allows B < E/R. 1 <= K <= min(E, 32); S >= 0; R*S*K < 2^31;
+ *   H, Hp multiples of 8 (bf16) or 4 (fp32).
+ * Size limits (MOONEP_ELIMIT): E <= 1024, R <= 1024, R*(E+B+1) <= 8192,
+ *   R*B <= 4096.
+ */
+int moonep_validate_shape(const moonep_shape* shape);
+
+/*
+ * Bytes of device workspace that moonep_plan and moonep_grouped_gemm need for
+ * `shape` (0 if the shape is invalid). One workspace serves every call of one
+ * layer; it also holds the sticky error word. Calls on one workspace must be
+ * ordered on one stream (they share it).
+ */
+size_t moonep_workspace_bytes(const moonep_shape* shape);
+
+/* Zero the workspace (enqueued on `stream`). Required once before first use. */
+int moonep_workspace_init(const moonep_shape* shape, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Plan the redundant experts for one router output and assign every (token, k)
+ * slot its place in its rank's static S*K buffer [maestro "The core idea:
+ * dynamic redundant experts", "The memory contract"; noticiai "A ideia central"].
+ *
+ *   topk_idx       in   int32 [N, K]: expert of slot u = g*K + k; a token names
+ *                       an expert at most once
+ *   cu_seqlens     out  int32 [R, E+B+1]: rank q's rows of its [E+B] weight view
+ *                       hold buffer positions [cu[q][i], cu[q][i+1]);
+ *                       cu[q][0] = 0, cu[q][E+B] = S*K
+ *   replica_expert out  int32 [R, B]: expert held by q's prefetch slot j, or -1
+ *   slot_map       out  int32 [N*K]: slot u -> q*SK + position in q's buffer
+ *   src_index      out  int32 [N*K]: inverse of slot_map
+ *
+ * The rule (the pages fix no planning algorithm, only its invariants):
+ *   T_e = slots routed to e, L_p = sum of T_e over p's home experts. Ranks with
+ *   L_p > SK donate, ranks with L_p < SK receive, both in ascending id: each
+ *   receiver takes all it lacks from the current donor; a donor that runs short
+ *   becomes a receiver of the next donor. A donor lays its experts out by
+ *   (T_e desc, e asc), hands its receivers consecutive ranges of that layout in
+ *   the order it gave them, and keeps the tail. A receiver numbers the distinct
+ *   experts of its range j = 0,1,..: j < B takes slot row E+j, j >= B reads the
+ *   home row e in place (inference overflow). Slots of one expert are ranked by
+ *   u; each row segment holds its slots in ascending u.
+ * Outputs are bit-exact and deterministic. Invalid router data (an id outside
+ * [0,E): MOONEP_ERR_ID_RANGE; the same id twice in a row: MOONEP_ERR_ID_DUP)
+ * sets the sticky error word; an out-of-range id also makes the plan empty
+ * (cu_seqlens all 0, replica_expert and slot_map and src_index all -1) so
+ * every later call of the layer does nothing out of bounds.
+ */
+int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, int32_t* cu_seqlens,
+                int32_t* replica_expert, int32_t* slot_map, int32_t* src_index,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fill every rank's prefetch slots: W_all[E + q*B + j] = W_all[replica_expert[q][j]]
+ * for every used slot [maestro "The memory contract": rows [E,E+B) are local
+ * prefetch slots filled by buffer.prefetch_weight; "The core idea": duplicated
+ * experts are prefetched before expert compute]. Unused slots are not touched.
+ *   w_all  in/out  dtype [E + R*B, H, Hp]
+ */
+int moonep_prefetch_weight(const moonep_shape* shape, const int32_t* replica_expert,
+                           void* w_all, void* stream);
+
+/*
+ * Fused permute: write each token row straight into its K expert-grouped
+ * positions of the ranks' S*K buffers [maestro "The core idea": zero copy,
+ * tokens written directly into their expert-grouped positions].
+ *   width  H (activations) or Hp (upstream gradients)
+ *   src    in   dtype [N, width]
+ *   gates  in   NULL, or float32 [N, K]: then row u is scaled by gates[u] in
+ *               float32 and rounded once to dtype (round to nearest even for
+ *               bfloat16) -- the backward permute of dY
+ *   dst    out  dtype [R*SK, width]: dst[slot_map[u]] = (gate *) src[u / K]
+ * Slots whose slot_map entry is negative are skipped.
+ */
+int moonep_dispatch(const moonep_shape* shape, int32_t width, const void* src,
+                    const int32_t* slot_map, const float* gates, void* dst, void* stream);
+
+/*
+ * Grouped GEMM over the [E+B, H, Hp] view, rows chosen only by cu_seqlens
+ * [maestro "The memory contract": the group GEMM addresses experts purely by
+ * row index and cu_seqlens selects the active rows]. Empty rows are skipped;
+ * nothing is synchronised with the host.
+ *   FWD    a = xp  dtype [R*SK, H],  b = w_all, c = out float32 [R*SK, Hp]:
+ *          c[rows of (q,i)] = a[rows] @ view_q(i)
+ *   DGRAD  a = dyp dtype [R*SK, Hp], b = w_all, c = dxp float32 [R*SK, H]:
+ *          c[rows of (q,i)] = a[rows] @ view_q(i)^T
+ *   WGRAD  a = xp, b = dyp; for each non-empty (q,i):
+ *          D = a[rows]^T @ b[rows] (float32 [H, Hp]);
+ *          i <  E: grad_home[i]         += D   (grad_home float32 [E, H, Hp])
+ *          i >= E: reduce_buf[q][i - E] += D   (reduce_buf float32 [R, B, H, Hp])
+ *          [maestro "The memory contract": fp32 grads mirror the weight layout,
+ *          rows [E,E+B) backed by a separate reduce buffer]. In training each
+ *          grad_home row is written by its home rank only, so there is no race.
+ * Inputs bf16 with float32 accumulation (MFMA), or float32 throughout.
+ * Requires H and Hp multiples of 64. DGRAD and WGRAD on an inference layer
+ * return MOONEP_EMODE.
+ */
+int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const void* a, const void* b,
+                        const int32_t* cu_seqlens, float* c, float* grad_home, float* reduce_buf,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fused unpermute: dst[g] = sum over k ascending of gates[g][k] * src[slot_map[g*K+k]]
+ * (gates NULL: weight 1 -- the unpermute of dX), float32 [maestro "The core
+ * idea": fused permute/unpermute].
+ *   src  in  float32 [R*SK, width];  dst  out  float32 [N, width]
+ * Slots whose slot_map entry is negative contribute nothing.
+ */
+int moonep_combine(const moonep_shape* shape, int32_t width, const float* src,
+                   const int32_t* slot_map, const float* gates, float* dst, void* stream);
+
+/*
+ * Fold replica gradients home [maestro "The memory contract": reduce_grad reads
+ * each rank's own experts' slots from every rank, accumulates into the local
+ * parameter grad and zeroes the consumed slots; spaxe 9]:
+ *   for q ascending, j ascending with e = replica_expert[q][j] >= 0:
+ *     grad_home[e] += reduce_buf[q][j]; reduce_buf[q][j] = 0
+ *   reduce_buf  in/out float32 [R, B, H, Hp]; grad_home in/out float32 [E, H, Hp]
+ * Unused slots are neither read nor written. Training layers only.
+ */
+int moonep_reduce_grad(const moonep_shape* shape, const int32_t* replica_expert,
+                       float* reduce_buf, float* grad_home, void* stream);
+
+/*
+ * Read (and if `clear`, reset) the sticky device error word of a workspace.
+ * Synchronises the device: for tests and debugging, not for the hot path.
+ */
+int moonep_get_error(const moonep_shape* shape, void* ws, size_t ws_bytes, int32_t* host_flags,
+                     int32_t clear);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOONEP_H */

@@ -173,3 +173,28 @@ def reduce_grad(replica_expert, reduce_buf, grad_home):
             if e >= 0:
                 grad_home[e] += reduce_buf[q, j]
                 reduce_buf[q, j] = 0
+
+
+# ----------------------------------------------------------------- sampled checks
+
+def dense_expert_outputs(x, W, topk_idx) -> np.ndarray:
+    """out(u) = x[g] @ W[e(u)] for every slot u = g*K + k of the given tokens: [N*K, H'].
+
+    ``W`` only needs ``W[e]`` for the experts these tokens use (it may fetch lazily)."""
+    x = np.asarray(x, dtype=np.float64)
+    topk = np.asarray(topk_idx)
+    N, K = topk.shape
+    Hp = W[int(topk.flat[0])].shape[1] if topk.size else 0
+    out = np.zeros((N * K, Hp), dtype=np.float64)
+    for e in np.unique(topk):
+        tok, kk = np.nonzero(topk == e)
+        out[tok * K + kk] = x[tok] @ np.asarray(W[int(e)], dtype=np.float64)
+    return out
+
+
+def wgrad_entries(x_rows, d_rows, hh, pp) -> np.ndarray:
+    """Entries (hh[i], pp[j]) of sum over slots of one expert of outer(x[g], d(u)),
+    given that expert's rows x_rows [n, H] and gated upstream rows d_rows [n, H']."""
+    xs = np.asarray(x_rows, dtype=np.float64)[:, hh]
+    ds = np.asarray(d_rows, dtype=np.float64)[:, pp]
+    return xs.T @ ds

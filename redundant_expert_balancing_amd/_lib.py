@@ -1,0 +1,164 @@
+"""Thin ctypes binding of libmoonep.so (include/moonep.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors give device pointers, torch's current
+stream gives the HIP stream. Every computation runs in the library's HIP
+kernels; there is no fallback, and a missing library raises at import of the
+first call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoonep.so")
+
+TRAIN, INFER = 0, 1
+BF16, FP32 = 0, 1
+FWD, DGRAD, WGRAD = 0, 1, 2
+ERR_ID_RANGE, ERR_ID_DUP = 1, 2
+OK, EINVAL, EWORKSPACE, EHIP, EMODE, ELIMIT = 0, -1, -2, -3, -4, -5
+
+# every symbol the header declares
+EXPORTS = (
+    "moonep_version", "moonep_strerror", "moonep_validate_shape", "moonep_workspace_bytes",
+    "moonep_workspace_init", "moonep_plan", "moonep_prefetch_weight", "moonep_dispatch",
+    "moonep_grouped_gemm", "moonep_combine", "moonep_reduce_grad", "moonep_get_error",
+)
+
+
+class Shape(ctypes.Structure):
+    """moonep_shape."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("R", "S", "E", "K", "B", "H", "Hp", "mode", "dtype")]
+
+    @classmethod
+    def of(cls, cfg) -> "Shape":
+        """From a LayerConfig-like object (R, S, E, K, B, H, Hp, mode, dtype strings)."""
+        return cls(cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.H, cfg.Hp,
+                   TRAIN if cfg.mode == "train" else INFER,
+                   BF16 if cfg.dtype == "bf16" else FP32)
+
+
+class MoonepError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+        self.status = status
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sp = ctypes.POINTER(Shape)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m redundant_expert_balancing_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moonep_version": ([], ctypes.c_int),
+            "moonep_strerror": ([ctypes.c_int], ctypes.c_char_p),
+            "moonep_validate_shape": ([_sp], ctypes.c_int),
+            "moonep_workspace_bytes": ([_sp], ctypes.c_size_t),
+            "moonep_workspace_init": ([_sp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+            "moonep_plan": ([_sp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+            "moonep_prefetch_weight": ([_sp, _vp, _vp, _vp], ctypes.c_int),
+            "moonep_dispatch": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "moonep_grouped_gemm": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp], ctypes.c_int),
+            "moonep_combine": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "moonep_reduce_grad": ([_sp, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "moonep_get_error": ([_sp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.c_int32], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moonep_strerror(status).decode()
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return _vp(getattr(stream, "cuda_stream", stream))
+
+
+def _check(fn: str, st: int) -> int:
+    if st != OK:
+        raise MoonepError(fn, st)
+    return st
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def moonep_version() -> int:
+    return lib().moonep_version()
+
+
+def moonep_validate_shape(shape: Shape) -> int:
+    return lib().moonep_validate_shape(ctypes.byref(shape))
+
+
+def moonep_workspace_bytes(shape: Shape) -> int:
+    return lib().moonep_workspace_bytes(ctypes.byref(shape))
+
+
+def moonep_workspace_init(shape, ws, stream=None):
+    _check("moonep_workspace_init",
+           lib().moonep_workspace_init(ctypes.byref(shape), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def moonep_plan(shape, topk_idx, cu_seqlens, replica_expert, slot_map, src_index, ws, stream=None):
+    _check("moonep_plan", lib().moonep_plan(
+        ctypes.byref(shape), _p(topk_idx), _p(cu_seqlens), _p(replica_expert), _p(slot_map),
+        _p(src_index), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def moonep_prefetch_weight(shape, replica_expert, w_all, stream=None):
+    _check("moonep_prefetch_weight", lib().moonep_prefetch_weight(
+        ctypes.byref(shape), _p(replica_expert), _p(w_all), _s(stream)))
+
+
+def moonep_dispatch(shape, width, src, slot_map, gates, dst, stream=None):
+    _check("moonep_dispatch", lib().moonep_dispatch(
+        ctypes.byref(shape), int(width), _p(src), _p(slot_map), _p(gates), _p(dst), _s(stream)))
+
+
+def moonep_grouped_gemm(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, ws, stream=None):
+    _check("moonep_grouped_gemm", lib().moonep_grouped_gemm(
+        ctypes.byref(shape), int(op), _p(a), _p(b), _p(cu_seqlens), _p(c), _p(grad_home),
+        _p(reduce_buf), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def moonep_combine(shape, width, src, slot_map, gates, dst, stream=None):
+    _check("moonep_combine", lib().moonep_combine(
+        ctypes.byref(shape), int(width), _p(src), _p(slot_map), _p(gates), _p(dst), _s(stream)))
+
+
+def moonep_reduce_grad(shape, replica_expert, reduce_buf, grad_home, stream=None):
+    _check("moonep_reduce_grad", lib().moonep_reduce_grad(
+        ctypes.byref(shape), _p(replica_expert), _p(reduce_buf), _p(grad_home), _s(stream)))
+
+
+def moonep_get_error(shape, ws, clear: bool = False) -> int:
+    flags = ctypes.c_int32(0)
+    _check("moonep_get_error", lib().moonep_get_error(
+        ctypes.byref(shape), _p(ws), _nbytes(ws), ctypes.byref(flags), int(clear)))
+    return flags.value

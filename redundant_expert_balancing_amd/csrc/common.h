@@ -1,0 +1,61 @@
+// Internal definitions shared by the HIP sources of the moonep library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moonep.h"
+
+namespace moonep {
+
+// Router tokens per planning chunk: one 64-wide wavefront owns a chunk, one lane
+// per token while counting, 64 consecutive slots per step while assigning.
+constexpr int kChunkTokens = 64;
+// Smallest GEMM M tile; sizes the tile list in the workspace.
+constexpr int kMinTileM = 64;
+
+// Sticky error word and per-call words at the head of the workspace.
+enum FlagWord { kFlagError = 0, kFlagPlanValid = 1, kFlagTileCount = 2, kFlagWords = 64 };
+
+struct WsLayout {
+  size_t flags, T, counts, piece_ptr, piece_tlo, piece_base, tiles, total;
+  int64_t nchunk, max_pieces, max_tiles;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(const moonep_shape& s) {
+  WsLayout w{};
+  const int64_t N = int64_t(s.R) * s.S;
+  const int64_t SK = int64_t(s.S) * s.K;
+  w.nchunk = (N + kChunkTokens - 1) / kChunkTokens;
+  w.max_pieces = int64_t(s.E) + 2 * int64_t(s.R) + 8;
+  w.max_tiles = int64_t(s.R) * ((SK + kMinTileM - 1) / kMinTileM + s.E + s.B) + 1;
+  size_t o = 0;
+  w.flags = o;      o = align256(o + kFlagWords * 4);
+  w.T = o;          o = align256(o + size_t(s.E) * 4);
+  w.counts = o;     o = align256(o + size_t(w.nchunk) * s.E * 4);
+  w.piece_ptr = o;  o = align256(o + size_t(s.E + 1) * 4);
+  w.piece_tlo = o;  o = align256(o + size_t(w.max_pieces) * 4);
+  w.piece_base = o; o = align256(o + size_t(w.max_pieces) * 4);
+  w.tiles = o;      o = align256(o + size_t(w.max_tiles) * 16);
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+inline T* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Host-side validation shared by all entry points (defined in api.cpp).
+int validate(const moonep_shape* s);
+int elem_bytes(const moonep_shape& s);
+int launch_status();  // MOONEP_OK or MOONEP_EHIP after the last launch
+
+}  // namespace moonep

@@ -1,0 +1,479 @@
+// On-GPU redundant-expert planner for gfx950.
+//
+// Plans a few duplicated experts from the current router output so that every
+// rank receives exactly S*K token-slots, and gives every slot its place in its
+// rank's static S*K buffer [ai-maestro.online "Moonshot AI open-sources MoonEP",
+// sections "The core idea: dynamic redundant experts" and "The memory
+// contract"]. The pages fix only the invariants; the rule implemented is stated
+// in moonep.h (moonep_plan). Four launches, no host synchronisation:
+//
+//   count   one wavefront per chunk of 64 tokens: per-chunk expert histogram
+//           (LDS atomics) into counts[chunk][E]; flags bad or repeated ids.
+//   scan    column-wise exclusive prefix of counts over chunks (the base rank
+//           of each chunk's first slot of every expert), T[e] = column total.
+//   solve   one workgroup: rank loads, donor tree, per-donor expert layout,
+//           pieces, prefetch slots, cu_seqlens and a per-expert piece table
+//           (first rank t and destination base of every piece).
+//   assign  one wavefront per chunk again: the stable rank t of every slot
+//           within its expert = chunk base + rank among equal ids in earlier
+//           64-slot steps (LDS counter) + rank among equal ids in the same step
+//           (wavefront match built from ballots); then slot_map / src_index.
+#include "common.h"
+
+namespace moonep {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kSolveThreads = 1024;
+
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan across a 1024-thread block; *total gets the block sum.
+__device__ inline int block_excl_scan(int v, int* swave, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) swave[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int x = lane < kSolveThreads / 64 ? swave[lane] : 0;
+    const int xi = wave_incl_scan(x);
+    if (lane < kSolveThreads / 64) swave[lane] = xi - x;
+    if (lane == kSolveThreads / 64 - 1) swave[kSolveThreads / 64] = xi;
+  }
+  __syncthreads();
+  const int r = swave[w] + incl - v;
+  *total = swave[kSolveThreads / 64];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------- count
+__global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restrict__ topk, int N,
+                                                         int K, int E, int nchunk,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ flags) {
+  extern __shared__ int32_t lds[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int32_t* hist = lds + w * E;
+  for (int e = lane; e < E; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * kWavesPerBlock + w;
+  int err = 0;
+  const int g = c * kChunkTokens + lane;
+  if (c < nchunk && g < N) {
+    const int32_t* row = topk + int64_t(g) * K;
+    for (int k = 0; k < K; ++k) {
+      const int e = row[k];
+      if (e < 0 || e >= E) {
+        err |= MOONEP_ERR_ID_RANGE;
+        continue;
+      }
+      for (int k2 = 0; k2 < k; ++k2)
+        if (row[k2] == e) err |= MOONEP_ERR_ID_DUP;
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  if (c < nchunk)
+    for (int e = lane; e < E; e += 64) counts[int64_t(c) * E + e] = hist[e];
+  if (err) atomicOr(&flags[kFlagError], err);
+}
+
+// ---------------------------------------------------------------- scan
+// Block: 64 experts (lanes) x 16 wavefronts, each wavefront a range of chunks.
+__global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ counts, int nchunk,
+                                                         int E, int32_t* __restrict__ T) {
+  __shared__ int32_t part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int per = (nchunk + 15) / 16;
+  const int c0 = w * per, c1 = min(nchunk, c0 + per);
+  int s = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) s += counts[int64_t(c) * E + e];
+  part[w][lane] = s;
+  __syncthreads();
+  if (w == 0) {
+    int run = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int v = part[i][lane];
+      part[i][lane] = run;
+      run += v;
+    }
+    if (e < E) T[e] = run;
+  }
+  __syncthreads();
+  int run = part[w][lane];
+  if (e < E)
+    for (int c = c0; c < c1; ++c) {
+      const int64_t idx = int64_t(c) * E + e;
+      const int v = counts[idx];
+      counts[idx] = run;
+      run += v;
+    }
+}
+
+// ---------------------------------------------------------------- solve
+struct SolveArgs {
+  int R, S, E, K, B, G, SK;
+  int64_t NK;
+  const int32_t* T;
+  int32_t* cu;        // [R, E+B+1]
+  int32_t* replica;   // [R, B]
+  int32_t* piece_ptr, *piece_tlo, *piece_base;
+  int32_t* flags;
+};
+
+// LDS carve-up of the solve kernel (ints).
+struct SolveLds {
+  int T, seqpos, off, seq, npiece, hot, parent, L, gchild, gamt, gdonor, glo, gfirst, dptr,
+      dfill, homestart, rowlen, swave, misc, total;
+  __host__ __device__ SolveLds(int R, int E, int B) {
+    int o = 0;
+    T = o; o += E;
+    seqpos = o; o += E;
+    off = o; o += E;
+    seq = o; o += E;
+    npiece = o; o += E;
+    hot = o; o += R;
+    parent = o; o += R;
+    L = o; o += R;
+    gchild = o; o += R;
+    gamt = o; o += R;
+    gdonor = o; o += R;
+    glo = o; o += R;
+    gfirst = o; o += R;
+    dptr = o; o += R + 1;
+    dfill = o; o += R;
+    homestart = o; o += R;
+    rowlen = o; o += R * (E + B);
+    swave = o; o += kSolveThreads / 64 + 1;
+    misc = o; o += 8;
+    total = o;
+  }
+};
+
+// Intersect expert e's layout interval with donor p's gift ranges and home tail.
+// Calls f(dest_rank, row, t_lo, t_hi) for each non-empty piece in t order.
+template <typename F>
+__device__ inline void for_each_piece(const SolveArgs& a, const int* sm, const SolveLds& L, int e,
+                                      F&& f) {
+  const int p = e / a.G;
+  const int off = sm[L.off + e], t = sm[L.T + e];
+  for (int gi = sm[L.dptr + p]; gi < sm[L.dptr + p + 1]; ++gi) {
+    const int lo = sm[L.glo + gi], hi = lo + sm[L.gamt + gi];
+    const int x = max(lo, off), y = min(hi, off + t);
+    if (x < y) {
+      const int j = sm[L.seqpos + e] - sm[L.gfirst + gi];
+      const int row = j < a.B ? a.E + j : e;  // j >= B: overflow, home row in place
+      f(sm[L.gchild + gi], row, x - off, y - off, j);
+    }
+  }
+  const int x = max(sm[L.homestart + p], off), y = min(sm[L.L + p], off + t);
+  if (x < y) f(p, e, x - off, y - off, -1);
+}
+
+__global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) {
+  extern __shared__ int sm[];
+  const SolveLds L(a.R, a.E, a.B);
+  const int tid = threadIdx.x;
+  const int EB = a.E + a.B;
+
+  __shared__ unsigned long long s_total;
+  if (tid == 0) s_total = 0;
+  __syncthreads();
+  unsigned long long part = 0;
+  for (int e = tid; e < a.E; e += kSolveThreads) {
+    sm[L.T + e] = a.T[e];
+    part += a.T[e];
+  }
+  atomicAdd(&s_total, part);
+  for (int i = tid; i < a.R * EB; i += kSolveThreads) sm[L.rowlen + i] = 0;
+  for (int i = tid; i < a.R * a.B; i += kSolveThreads) a.replica[i] = -1;
+  __syncthreads();
+
+  if (s_total != (unsigned long long)a.NK) {  // an id outside [0,E): publish an empty plan
+    for (int i = tid; i < a.R * (EB + 1); i += kSolveThreads) a.cu[i] = 0;
+    for (int i = tid; i <= a.E; i += kSolveThreads) a.piece_ptr[i] = 0;
+    if (tid == 0) a.flags[kFlagPlanValid] = 0;
+    return;
+  }
+
+  // rank loads L_p
+  for (int p = tid; p < a.R; p += kSolveThreads) {
+    int s = 0;
+    for (int e = p * a.G; e < (p + 1) * a.G; ++e) s += sm[L.T + e];
+    sm[L.L + p] = s;
+  }
+  // layout of each group: position by (T desc, e asc)
+  for (int e = tid; e < a.E; e += kSolveThreads) {
+    const int p = e / a.G, te = sm[L.T + e];
+    int pos = 0;
+    for (int e2 = p * a.G; e2 < (p + 1) * a.G; ++e2) {
+      const int t2 = sm[L.T + e2];
+      pos += (t2 > te) || (t2 == te && e2 < e);
+    }
+    sm[L.seqpos + e] = pos;
+    sm[L.seq + p * a.G + pos] = e;
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kSolveThreads) {
+    const int p = e / a.G, pe = sm[L.seqpos + e];
+    int off = 0;
+    for (int s = 0; s < pe; ++s) off += sm[L.T + sm[L.seq + p * a.G + s]];
+    sm[L.off + e] = off;
+  }
+
+  // donor tree: sequential, R is small
+  if (tid == 0) {
+    int nhot = 0, ngift = 0;
+    for (int p = 0; p < a.R; ++p) {
+      sm[L.parent + p] = -1;
+      if (sm[L.L + p] > a.SK) sm[L.hot + nhot++] = p;
+    }
+    if (nhot > 0) {
+      int i = 0;
+      int avail = sm[L.L + sm[L.hot]] - a.SK;
+      for (int q = 0; q < a.R; ++q) {
+        const int lq = sm[L.L + q];
+        if (lq >= a.SK) continue;
+        const int need = a.SK - lq;
+        const int d = sm[L.hot + i];
+        sm[L.parent + q] = d;
+        sm[L.gdonor + ngift] = d; sm[L.gchild + ngift] = q; sm[L.gamt + ngift] = need; ++ngift;
+        avail -= need;
+        while (avail < 0 && i + 1 < nhot) {
+          const int cur = sm[L.hot + i], nxt = sm[L.hot + i + 1];
+          sm[L.parent + cur] = nxt;
+          sm[L.gdonor + ngift] = nxt; sm[L.gchild + ngift] = cur; sm[L.gamt + ngift] = -avail; ++ngift;
+          avail += sm[L.L + nxt] - a.SK;
+          ++i;
+        }
+        if (avail == 0 && i + 1 < nhot) {
+          ++i;
+          avail = sm[L.L + sm[L.hot + i]] - a.SK;
+        }
+      }
+    }
+    // group the gifts by donor, keeping the order they were made in
+    for (int p = 0; p <= a.R; ++p) sm[L.dptr + p] = 0;
+    for (int k = 0; k < ngift; ++k) sm[L.dptr + sm[L.gdonor + k] + 1]++;
+    for (int p = 0; p < a.R; ++p) sm[L.dptr + p + 1] += sm[L.dptr + p];
+    for (int p = 0; p < a.R; ++p) {
+      sm[L.dfill + p] = sm[L.dptr + p];
+      sm[L.homestart + p] = 0;
+    }
+    // second pass writes sorted copies after the raw lists (gfirst used as scratch)
+    int* child = sm + L.gfirst;  // temporary: child, reused below
+    int* amt = sm + L.glo;       // temporary: amount
+    for (int k = 0; k < ngift; ++k) {
+      const int d = sm[L.gdonor + k];
+      const int slot = sm[L.dfill + d]++;
+      child[slot] = sm[L.gchild + k];
+      amt[slot] = sm[L.gamt + k];
+    }
+    for (int k = 0; k < ngift; ++k) {
+      sm[L.gchild + k] = child[k];
+      sm[L.gamt + k] = amt[k];
+    }
+    // consecutive ranges of the donor's layout, starting at 0, in gift order
+    for (int p = 0; p < a.R; ++p) {
+      int start = 0;
+      for (int k = sm[L.dptr + p]; k < sm[L.dptr + p + 1]; ++k) {
+        sm[L.glo + k] = start;
+        start += sm[L.gamt + k];
+      }
+      sm[L.homestart + p] = start;
+    }
+    sm[L.misc] = ngift;
+  }
+  __syncthreads();
+
+  // layout position of the first expert each gift range touches
+  const int ngift = sm[L.misc];
+  for (int k = tid; k < ngift; k += kSolveThreads) {
+    int d = 0;
+    for (int p = 0; p < a.R; ++p)
+      if (k >= sm[L.dptr + p] && k < sm[L.dptr + p + 1]) d = p;
+    const int lo = sm[L.glo + k];
+    int s = 0;
+    while (s < a.G - 1) {
+      const int e = sm[L.seq + d * a.G + s];
+      if (sm[L.off + e] + sm[L.T + e] > lo) break;
+      ++s;
+    }
+    sm[L.gfirst + k] = s;
+  }
+  __syncthreads();
+
+  // pieces: row lengths, prefetch slots, piece counts
+  for (int e = tid; e < a.E; e += kSolveThreads) {
+    int n = 0;
+    for_each_piece(a, sm, L, e, [&](int q, int row, int tlo, int thi, int j) {
+      sm[L.rowlen + q * EB + row] = thi - tlo;
+      if (j >= 0 && j < a.B) a.replica[q * a.B + j] = e;
+      ++n;
+    });
+    sm[L.npiece + e] = n;
+  }
+  __syncthreads();
+
+  // cu_seqlens: exclusive prefix of row lengths per rank; rowlen becomes row start
+  {
+    const int lane = tid & 63, w = tid >> 6;
+    for (int q = w; q < a.R; q += kSolveThreads / 64) {
+      int carry = 0;
+      if (lane == 0) a.cu[q * (EB + 1)] = 0;
+      for (int base = 0; base < EB; base += 64) {
+        const int i = base + lane;
+        const int v = i < EB ? sm[L.rowlen + q * EB + i] : 0;
+        const int incl = wave_incl_scan(v);
+        if (i < EB) {
+          a.cu[q * (EB + 1) + i + 1] = carry + incl;
+          sm[L.rowlen + q * EB + i] = carry + incl - v;
+        }
+        carry += __shfl(incl, 63, 64);
+      }
+    }
+  }
+  int total_pieces;
+  const int my_np = tid < a.E ? sm[L.npiece + tid] : 0;
+  const int first = block_excl_scan(my_np, sm + L.swave, &total_pieces);
+  if (tid < a.E) sm[L.npiece + tid] = first;  // now the piece pointer
+  __syncthreads();
+
+  // piece table: per expert, pieces in t order with dest base = q*SK + row start - t_lo
+  for (int e = tid; e < a.E; e += kSolveThreads) {
+    int k = sm[L.npiece + e];
+    a.piece_ptr[e] = k;
+    for_each_piece(a, sm, L, e, [&](int q, int row, int tlo, int thi, int j) {
+      a.piece_tlo[k] = tlo;
+      a.piece_base[k] = q * a.SK + sm[L.rowlen + q * EB + row] - tlo;
+      ++k;
+    });
+  }
+  if (tid == 0) {
+    a.piece_ptr[a.E] = total_pieces;
+    a.flags[kFlagPlanValid] = 1;
+  }
+}
+
+// ---------------------------------------------------------------- assign
+__global__ __launch_bounds__(256) void plan_assign_kernel(
+    const int32_t* __restrict__ topk, int N, int K, int E, int nchunk, int nbits,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ piece_ptr,
+    const int32_t* __restrict__ piece_tlo, const int32_t* __restrict__ piece_base,
+    const int32_t* __restrict__ flags, int32_t* __restrict__ slot_map,
+    int32_t* __restrict__ src_index) {
+  extern __shared__ int32_t lds[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * kWavesPerBlock + w;
+  if (c >= nchunk) return;  // whole wavefront leaves; no block barrier follows
+  const int64_t NK = int64_t(N) * K;
+  const int64_t u0 = int64_t(c) * kChunkTokens * K;
+  const int64_t u1 = min(NK, u0 + int64_t(kChunkTokens) * K);
+  if (flags[kFlagPlanValid] == 0) {
+    for (int64_t u = u0 + lane; u < u1; u += 64) {
+      slot_map[u] = -1;
+      src_index[u] = -1;
+    }
+    return;
+  }
+  int32_t* run = lds + w * E;  // next rank of every expert inside this chunk
+  for (int e = lane; e < E; e += 64) run[e] = base[int64_t(c) * E + e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  for (int64_t s = u0; s < u1; s += 64) {
+    const int64_t u = s + lane;
+    const bool act = u < u1;
+    const int v = act ? topk[u] : 0;
+    // lanes holding the same expert id: intersect the ballots of every id bit
+    uint64_t m = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (v >> b) & 1;
+      const uint64_t bal = __ballot(act && bit);
+      m &= bit ? bal : ~bal;
+    }
+    int old = 0;
+    const uint64_t below = m & lt_mask;
+    if (act && below == 0) old = atomicAdd(&run[v], __popcll(m));  // group leader
+    const int leader = act ? __ffsll((unsigned long long)m) - 1 : lane;
+    const int grp_base = __shfl(old, leader, 64);
+    if (act) {
+      const int t = grp_base + __popcll(below);
+      int p = piece_ptr[v];
+      const int p1 = piece_ptr[v + 1];
+      while (p + 1 < p1 && piece_tlo[p + 1] <= t) ++p;
+      const int dest = p < p1 ? piece_base[p] + t : -1;
+      slot_map[u] = dest;
+      if (dest >= 0 && int64_t(dest) < NK) src_index[dest] = int32_t(u);
+    }
+  }
+}
+
+}  // namespace moonep
+
+using namespace moonep;
+
+extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, int32_t* cu_seqlens,
+                           int32_t* replica_expert, int32_t* slot_map, int32_t* src_index, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int st = validate(shape);
+  if (st) return st;
+  const moonep_shape& s = *shape;
+  if (!aligned16(topk_idx) || !aligned16(cu_seqlens) || !aligned16(slot_map) ||
+      !aligned16(src_index) || !aligned16(ws))
+    return MOONEP_EINVAL;
+  if (s.B > 0 && !aligned16(replica_expert)) return MOONEP_EINVAL;
+  const WsLayout w = ws_layout(s);
+  if (ws_bytes < w.total) return MOONEP_EWORKSPACE;
+  hipStream_t strm = as_stream(stream);
+  const int N = s.R * s.S;
+  const int nchunk = int(w.nchunk);
+  int32_t* flags = ws_ptr<int32_t>(ws, w.flags);
+  int32_t* T = ws_ptr<int32_t>(ws, w.T);
+  int32_t* counts = ws_ptr<int32_t>(ws, w.counts);
+  int32_t* pptr = ws_ptr<int32_t>(ws, w.piece_ptr);
+  int32_t* ptlo = ws_ptr<int32_t>(ws, w.piece_tlo);
+  int32_t* pbase = ws_ptr<int32_t>(ws, w.piece_base);
+  const size_t chunk_lds = size_t(kWavesPerBlock) * s.E * 4;
+  const int chunk_blocks = (nchunk + kWavesPerBlock - 1) / kWavesPerBlock;
+
+  if (nchunk > 0) {
+    plan_count_kernel<<<chunk_blocks, 256, chunk_lds, strm>>>(topk_idx, N, s.K, s.E, nchunk,
+                                                              counts, flags);
+    if (launch_status()) return MOONEP_EHIP;
+  }
+  plan_scan_kernel<<<(s.E + 63) / 64, 1024, 0, strm>>>(counts, nchunk, s.E, T);
+  if (launch_status()) return MOONEP_EHIP;
+
+  SolveArgs a;
+  a.R = s.R; a.S = s.S; a.E = s.E; a.K = s.K; a.B = s.B; a.G = s.E / s.R; a.SK = s.S * s.K;
+  a.NK = int64_t(N) * s.K;
+  a.T = T; a.cu = cu_seqlens; a.replica = replica_expert;
+  a.piece_ptr = pptr; a.piece_tlo = ptlo; a.piece_base = pbase; a.flags = flags;
+  const size_t solve_lds = size_t(SolveLds(s.R, s.E, s.B).total) * 4;
+  if (solve_lds > 64 * 1024) return MOONEP_ELIMIT;
+  plan_solve_kernel<<<1, kSolveThreads, solve_lds, strm>>>(a);
+  if (launch_status()) return MOONEP_EHIP;
+
+  if (nchunk > 0) {
+    int nbits = 0;
+    while ((1 << nbits) < s.E) ++nbits;
+    plan_assign_kernel<<<chunk_blocks, 256, chunk_lds, strm>>>(
+        topk_idx, N, s.K, s.E, nchunk, nbits, counts, pptr, ptlo, pbase, flags, slot_map,
+        src_index);
+    if (launch_status()) return MOONEP_EHIP;
+  }
+  return MOONEP_OK;
+}

@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every symbol include/moonep.h declares, and
+validates shapes and arguments on the host (no GPU call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from redundant_expert_balancing_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moonep.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moonep_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    declared = _declared()
+    assert declared == sorted(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert L.moonep_version() >= 100
+    for st in (L.OK, L.EINVAL, L.EWORKSPACE, L.EHIP, L.EMODE, L.ELIMIT):
+        assert L.strerror(st) and L.strerror(st) != "unknown status"
+    assert L.strerror(12345) == "unknown status"
+
+
+def S(**kw):
+    base = dict(R=4, S=64, E=16, K=2, B=4, H=128, Hp=64, mode=L.TRAIN, dtype=L.BF16)
+    base.update(kw)
+    return L.Shape(*[base[k] for k in ("R", "S", "E", "K", "B", "H", "Hp", "mode", "dtype")])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, L.OK),
+    (dict(S=0), L.OK),                          # empty layer is valid
+    (dict(mode=L.INFER, B=0), L.OK),
+    (dict(mode=L.INFER, B=3), L.OK),
+    (dict(E=18), L.EINVAL),                     # E % R != 0
+    (dict(B=3), L.EINVAL),                      # training needs B = E/R
+    (dict(mode=L.INFER, B=5), L.EINVAL),        # B > E/R
+    (dict(K=17), L.EINVAL),                     # K > E
+    (dict(K=0), L.EINVAL),
+    (dict(H=100), L.EINVAL),                    # not a multiple of 8 (bf16)
+    (dict(H=100, dtype=L.FP32), L.OK),          # multiple of 4 is enough for fp32
+    (dict(Hp=6, dtype=L.FP32), L.EINVAL),
+    (dict(R=8, S=1 << 27, E=64, K=8, B=8), L.EINVAL),   # R*S*K >= 2^31
+    (dict(mode=7), L.EINVAL),
+    (dict(dtype=3), L.EINVAL),
+    (dict(R=1, E=2048, B=2048, K=8), L.ELIMIT),           # E > 1024
+    (dict(R=64, E=256, B=4), L.ELIMIT),                   # R*(E+B+1) > 8192
+])
+def test_validate_shape(kw, status):
+    assert L.moonep_validate_shape(S(**kw)) == status
+
+
+def test_workspace_bytes():
+    assert L.moonep_workspace_bytes(S(E=18)) == 0
+    small = L.moonep_workspace_bytes(S())
+    big = L.moonep_workspace_bytes(S(S=6400))
+    assert 0 < small < big and small % 256 == 0
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    lib = L.lib()
+    sh = S()
+    ws = ctypes.c_void_p(0)
+    st = lib.moonep_plan(ctypes.byref(sh), None, None, None, None, None, ws, 0, None)
+    assert st == L.EINVAL
+    p = ctypes.c_void_p(0x1000)       # aligned but never dereferenced: rejected for ws size
+    st = lib.moonep_plan(ctypes.byref(sh), p, p, p, p, p, p, 16, None)
+    assert st == L.EWORKSPACE
+    bad = ctypes.c_void_p(0x1004)     # misaligned
+    assert lib.moonep_plan(ctypes.byref(sh), bad, p, p, p, p, p, 1 << 30, None) == L.EINVAL
+    assert lib.moonep_dispatch(ctypes.byref(sh), 100, p, p, None, p, None) == L.EINVAL  # width
+    assert lib.moonep_combine(ctypes.byref(sh), 64, bad, p, None, p, None) == L.EINVAL
+    assert lib.moonep_grouped_gemm(ctypes.byref(sh), 7, p, p, p, p, None, None, p, 1 << 30, None) == L.EINVAL
+    inf = S(mode=L.INFER, B=2)
+    assert lib.moonep_grouped_gemm(ctypes.byref(inf), L.DGRAD, p, p, p, p, None, None, p, 1 << 30, None) == L.EMODE
+    assert lib.moonep_reduce_grad(ctypes.byref(inf), p, p, p, None) == L.EMODE
+    odd = S(H=96, Hp=64)              # bf16 GEMM needs multiples of 64
+    assert lib.moonep_grouped_gemm(ctypes.byref(odd), L.FWD, p, p, p, p, None, None, p, 1 << 30, None) == L.EINVAL

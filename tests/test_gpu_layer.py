@@ -1,0 +1,209 @@
+"""GPU value parity of the whole path: plan -> prefetch_weight -> dispatch ->
+grouped GEMM -> combine, and the backward (gated dispatch of dY, dgrad, wgrad,
+unpermute, reduce_grad), against the float64 oracle on the same inputs.
+
+Small layers are compared element by element everywhere; the full-size layers on
+sampled tokens and experts (the oracle computes those one by one), plus
+properties that hold at any size (the permuted buffers are exact copies, the
+prefetch slots equal their home rows, home rows are never written, consumed
+replica-gradient slots end at zero). Tolerances: max abs error <= 1e-2 *
+RMS(reference) for bf16 layers, <= 1e-5 * RMS(reference) for fp32 layers.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as M
+from oracle import plan as P
+from redundant_expert_balancing_amd.layer import MoEProjection
+from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
+
+from gpu_helpers import LazyW, assert_plan_equal, rel_err, say, small_cfg, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(cfg, target, backward=False, alpha=None, seed=0):
+    r = make_routing(cfg, target, seed=seed, alpha=alpha)
+    d = make_dense(cfg, "cuda", seed, which=("x", "W", "dy") if backward else ("x", "W"),
+                   w_rows=cfg.E + cfg.R * cfg.B)
+    layer = MoEProjection(cfg, "cuda", backward=backward, w_all=d["W"])
+    topk = torch.from_numpy(r.topk_idx).cuda()
+    gates = torch.from_numpy(r.gates).cuda()
+    return r, layer, d, topk, gates
+
+
+def _host(t):
+    return t.float().cpu().numpy()
+
+
+def _poison_forward(layer):
+    layer.xp.view(torch.int16).fill_(-1)      # bf16 / fp32 NaN patterns
+    layer.out.fill_(float("nan"))
+    layer.y.fill_(float("nan"))
+
+
+def _check_permuted_copy(layer, x, slot_map, K):
+    """xp[slot_map[u]] == x[u // K] bit for bit, for every slot."""
+    sm = slot_map.long()
+    src = torch.arange(sm.numel(), device=sm.device) // K
+    assert torch.equal(layer.xp[sm], x[src])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_train", "bf16_train_mild"])
+def test_forward_full_compare(name):
+    cfg = CONFIGS[name]
+    target = cfg.maxvio[0]
+    say("forward full", name)
+    r, layer, d, topk, gates = _setup(cfg, target)
+    _poison_forward(layer)
+    w_home = d["W"][:cfg.E].clone()
+    y = layer.forward(topk, d["x"], gates)
+    torch.cuda.synchronize()
+    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    assert_plan_equal({"cu_seqlens": layer.cu_seqlens.cpu().numpy(),
+                       "replica_expert": layer.replica_expert[:, :cfg.B].cpu().numpy(),
+                       "slot_map": layer.slot_map.cpu().numpy(),
+                       "src_index": layer.src_index.cpu().numpy()}, pl)
+    assert torch.equal(d["W"][:cfg.E], w_home)
+    x_h, W_h = _host(d["x"]), _host(w_home)
+    # prefetch slots hold exact copies of their experts
+    for q in range(cfg.R):
+        for j in range(cfg.B):
+            e = int(pl.replica_expert[q, j])
+            if e >= 0:
+                assert torch.equal(layer.w_all[cfg.E + q * cfg.B + j], w_home[e])
+    _check_permuted_copy(layer, d["x"], layer.slot_map, cfg.K)
+    # GEMM output of every slot, and the combined output, against the oracle
+    out_ref = M.dense_expert_outputs(x_h, W_h, r.topk_idx)            # [N*K, H'] by slot u
+    out_got = _host(layer.out)[pl.slot_map]
+    assert rel_err(out_got, out_ref) <= tolerance(cfg)
+    y_ref = M.dense_forward(x_h, W_h, r.topk_idx, r.gates)
+    e = rel_err(_host(y), y_ref)
+    say("forward full", name, "max err / RMS", e)
+    assert e <= tolerance(cfg)
+
+
+@pytest.mark.parametrize("key", [("bench_shape", 0.2), ("bench_shape", 1.0), ("bench_shape", 10.0),
+                                 ("bench_shape", 20.0), ("infer_overflow", 10.0)],
+                         ids=lambda k: f"{k[0]}-{k[1]}")
+def test_forward_full_size_sampled(key):
+    name, target = key
+    cfg = CONFIGS[name]
+    say("forward sampled", name, target)
+    r, layer, d, topk, gates = _setup(cfg, target)
+    w_home = d["W"][:cfg.E].clone()
+    _poison_forward(layer)
+    y = layer.forward(topk, d["x"], gates)
+    torch.cuda.synchronize()
+    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    assert np.array_equal(layer.slot_map.cpu().numpy(), pl.slot_map)
+    assert np.array_equal(layer.cu_seqlens.cpu().numpy(), pl.cu_seqlens)
+    if cfg.mode == "infer":
+        assert pl.n_overflow >= 1
+    assert torch.equal(d["W"][:cfg.E], w_home)
+    for q in range(cfg.R):
+        for j in range(cfg.B):
+            e = int(pl.replica_expert[q, j])
+            if e >= 0:
+                assert torch.equal(layer.w_all[cfg.E + q * cfg.B + j], w_home[e])
+    _check_permuted_copy(layer, d["x"], layer.slot_map, cfg.K)
+    # sampled tokens: spread over all ranks, plus tokens routed to replicated and
+    # overflow experts (their slots land in prefetch rows or remote home rows)
+    rng = np.random.default_rng(1)
+    N = cfg.R * cfg.S
+    pick = set(rng.choice(N, 12, replace=False).tolist())
+    rep_experts = set(int(e) for e in pl.replica_expert.ravel() if e >= 0)
+    for e in sorted(rep_experts)[:4]:
+        pick.add(int(np.nonzero((r.topk_idx == e).any(axis=1))[0][-1]))
+    for e in range(cfg.E):     # overflow pieces: rows e < E on a non-home rank
+        for (q, row, tlo, thi) in pl.pieces[e]:
+            if row < cfg.E and q != e // cfg.G:
+                toks = np.nonzero((r.topk_idx == e).any(axis=1))[0]
+                pick.add(int(toks[tlo]))
+    toks = np.array(sorted(pick))
+    W = LazyW(w_home)
+    x_s = _host(d["x"][torch.from_numpy(toks).cuda()])
+    out_ref = M.dense_expert_outputs(x_s, W, r.topk_idx[toks])
+    slots = (toks[:, None] * cfg.K + np.arange(cfg.K)[None, :]).ravel()
+    out_got = _host(layer.out[torch.from_numpy(pl.slot_map[slots]).long().cuda()])
+    assert rel_err(out_got, out_ref) <= tolerance(cfg)
+    y_ref = M.dense_forward(x_s, W, r.topk_idx[toks], r.gates[toks])
+    e = rel_err(_host(y[torch.from_numpy(toks).cuda()]), y_ref)
+    say("forward sampled", name, target, len(toks), "tokens, max err / RMS", e)
+    assert e <= tolerance(cfg)
+
+
+def _backward_check(cfg, target, alpha=None, full=False):
+    say("backward", cfg.name, target, "full" if full else "sampled")
+    r, layer, d, topk, gates = _setup(cfg, target, backward=True, alpha=alpha)
+    g0 = torch.Generator(device="cuda").manual_seed(123)
+    init = torch.randn(layer.grad_home.shape, generator=g0, device="cuda")
+    layer.grad_home.copy_(init)            # grads accumulate (+=) into whatever is there
+    layer.forward(topk, d["x"], gates)
+    layer.dyp.view(torch.int16).fill_(-1)
+    layer.dxp.fill_(float("nan"))
+    layer.dx.fill_(float("nan"))
+    dx = layer.backward(d["dy"], gates)
+    torch.cuda.synchronize()
+    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    assert pl.n_replicas > 0
+    # consumed replica-gradient slots end at exactly zero
+    assert int(torch.count_nonzero(layer.reduce_buf)) == 0
+    # gated permute of dY: one fp32 product, one rounding; exact at every slot
+    sm = layer.slot_map.long()
+    u = torch.arange(sm.numel(), device="cuda")
+    want = (gates.reshape(-1)[u][:, None] * d["dy"].float()[u // cfg.K]).to(layer.dtype)
+    assert torch.equal(layer.dyp[sm], want)
+    N = cfg.R * cfg.S
+    rng = np.random.default_rng(2)
+    toks = np.arange(N) if full else np.sort(rng.choice(N, 16, replace=False))
+    tk = torch.from_numpy(toks).cuda()
+    W = LazyW(d["W"][:cfg.E])
+    x_s, dy_s = _host(d["x"][tk]), _host(d["dy"][tk])
+    dd = M.gated_dy(dy_s, r.gates[toks], cfg.dtype)
+    # dgrad oracle: dx[g] = sum_k d(g,k) @ W[e]^T
+    if full:
+        dx_ref, _ = M.dense_backward(x_s, np.stack([W[e] for e in range(cfg.E)]),
+                                     r.topk_idx[toks], dd)
+    else:
+        dx_ref = np.zeros((len(toks), cfg.H))
+        for i, g in enumerate(toks):
+            for k in range(cfg.K):
+                w_e = W[r.topk_idx[g, k]].astype(np.float64)
+                dx_ref[i] += dd[i * cfg.K + k].astype(np.float64) @ w_e.T
+    e = rel_err(_host(dx[tk]), dx_ref)
+    say("backward dx err", e)
+    assert e <= tolerance(cfg)
+    # weight gradients: replicated experts (gradient folded home) and a few others
+    experts = sorted(set(int(x) for x in pl.replica_expert.ravel() if x >= 0))[:6]
+    experts += [int(x) for x in rng.choice(cfg.E, 3, replace=False) if x not in experts]
+    hh = rng.choice(cfg.H, 24, replace=False)
+    pp = rng.choice(cfg.Hp, 24, replace=False)
+    gh = layer.grad_home
+    for ex in experts:
+        tok, kk = np.nonzero(r.topk_idx == ex)
+        if len(tok) == 0:
+            continue
+        t_dev = torch.from_numpy(tok).cuda()
+        x_rows = _host(d["x"][t_dev][:, torch.from_numpy(hh).cuda()])
+        dy_rows = _host(d["dy"][t_dev][:, torch.from_numpy(pp).cuda()])
+        d_all = M.gated_dy(dy_rows, r.gates[tok], cfg.dtype)          # [n*K, |pp|]
+        d_rows = d_all[np.arange(len(tok)) * cfg.K + kk]
+        ref = _host(init[ex][torch.from_numpy(hh).cuda()][:, torch.from_numpy(pp).cuda()]) + \
+            M.wgrad_entries(x_rows, d_rows, np.arange(len(hh)), np.arange(len(pp)))
+        got = _host(gh[ex][torch.from_numpy(hh).cuda()][:, torch.from_numpy(pp).cuda()])
+        scale = M.wgrad_entries(x_rows, d_rows, np.arange(len(hh)), np.arange(len(pp)))
+        err = float(np.abs(got - ref).max() / max(np.sqrt(np.mean(scale ** 2)), 1e-30))
+        say("backward dW expert", ex, "slots", len(tok), "err", err)
+        assert err <= tolerance(cfg)
+
+
+def test_backward_full_size_sampled():
+    _backward_check(CONFIGS["train_backward"], 15.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_small_full_compare(dtype):
+    cfg = small_cfg(name=f"bwd_small_{dtype}", R=4, S=96, E=16, K=4, H=128, Hp=192, dtype=dtype)
+    _backward_check(cfg, 3.0, alpha=2.5, full=True)
