@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the balanced expert-parallel MoE layer on one MI355X.
+
+One step = one pass of the whole forward hot path over one batch of synthetic
+router output at the pages' bench shape (R=8 ranks, S=8192 tokens per rank,
+E=384 experts, K=8, B=48 prefetch slots, H=7168, H'=2048, bf16):
+plan -> prefetch_weight -> dispatch -> grouped GEMM -> combine. Steps cycle over
+the four router imbalance points maxvio in {0.2, 1, 10, 20}, all drawn from one
+shared seed. Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0). Besides the contract fields:
+  roofline      the grouped GEMM (dominant kernel) against dense bf16 MFMA peak;
+                its average duration comes from HIP events around every GEMM
+                launch inside the timed region, on the stream it runs on;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
+  stages_us     per-stage median microseconds at every imbalance point
+                (each repetition after a 1 GiB write that evicts the caches);
+  hbm_stages    plan + dispatch + combine against the HBM peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + plan/dispatch us vs maxvio (S=8192,E=384,K=8,H=7168)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_bench_shape_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--config", default="bench_shape")
+    ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def gemm_source_sha() -> str:
+    with open(os.path.join(ROOT, "redundant_expert_balancing_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per GEMM launch from the committed counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha") != gemm_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(cfg, routing, x_dev, w_dev, n_tok: int = 24):
+    """The oracle as it stands, on the host: the full plan of one routing plus the
+    dense expert projection and gated combine of ``n_tok`` sampled tokens."""
+    import numpy as np
+    from oracle import moe as M
+    from oracle import plan as P
+
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    P.plan(routing.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    t_plan = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(cfg.N, n_tok, replace=False))
+    import torch
+    x_s = x_dev[torch.from_numpy(toks).cuda()].float().cpu().numpy()
+    experts = np.unique(routing.topk_idx[toks])
+    W = {int(e): w_dev[int(e)].float().cpu().numpy() for e in experts}   # inputs, fetched first
+
+    class Wmap:
+        shape = (cfg.E, cfg.H, cfg.Hp)
+
+        def __getitem__(self, e):
+            return W[int(e)]
+
+    t0 = time.perf_counter()
+    M.dense_forward(x_s, Wmap(), routing.topk_idx[toks], routing.gates[toks])
+    t_dense = time.perf_counter() - t0
+    per_token = t_plan / cfg.N + t_dense / n_tok
+    return {"value": round(1.0 / per_token, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"plan rule on the full {cfg.N}-token routing at maxvio "
+                       f"{routing.maxvio:.3g} ({t_plan:.2f} s, 1 thread) + float64 dense "
+                       f"projection and gated combine of {n_tok} sampled tokens "
+                       f"({t_dense:.2f} s, BLAS on {cores} cores); tokens/s = "
+                       "1 / (t_plan/N + t_dense/n_tok)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the R expert-parallel ranks are emulated as "
+              "partitions of one GPU's memory, so --gpus above 1 is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from redundant_expert_balancing_amd import _lib as L
+    from redundant_expert_balancing_amd.layer import MoEProjection
+    from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    L.lib()   # fail loudly if the HIP library is missing
+
+    cfg = CONFIGS[args.config]
+    print(f"[bench] {cfg.name}: generating routing for maxvio {cfg.maxvio}", file=sys.stderr, flush=True)
+    routings = [make_routing(cfg, t) for t in cfg.maxvio]
+    d = make_dense(cfg, "cuda", 0, which=("x", "W"), w_rows=cfg.E + cfg.R * cfg.B)
+    layer = MoEProjection(cfg, "cuda", w_all=d["W"])
+    x = d["x"]
+    topks = [torch.from_numpy(r.topk_idx).cuda() for r in routings]
+    gates = [torch.from_numpy(r.gates).cuda() for r in routings]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    N = cfg.N
+    n_pts = len(routings)
+
+    def step(i, ev=None):
+        j = i % n_pts
+        layer.plan(topks[j])
+        layer.prefetch()
+        layer.dispatch(x)
+        if ev is not None:
+            ev[0].record(stream)
+        layer.gemm_fwd()
+        if ev is not None:
+            ev[1].record(stream)
+        layer.combine(gates[j])
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    gemm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, gemm_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in gemm_ev]))
+    assert layer.error_flags() == 0
+
+    flops = 2.0 * cfg.H * cfg.Hp * N * cfg.K
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(), "kernel": "gemm_bf16_kernel (FWD)",
+                "avg_launch_ms": round(gemm_ms, 4), "flop_per_launch": flops}
+
+    out = {
+        "metric": METRIC,
+        "value": round(N * args.steps / (ms_total * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "R": cfg.R, "S": cfg.S, "E": cfg.E, "K": cfg.K,
+                   "B": cfg.B, "H": cfg.H, "Hp": cfg.Hp, "maxvio": list(cfg.maxvio),
+                   "mode": cfg.mode, "parallelism": f"ep{cfg.R} emulated on 1 GPU"},
+        "roofline": roofline,
+        "wall_s": round(wall, 3),
+    }
+
+    if not args.no_stages:
+        out["stages_us"], out["hbm_stages"] = stage_table(cfg, layer, x, topks, gates, routings,
+                                                          args.stage_reps)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, routings[-1], x, d["W"])
+    print(json.dumps(out), flush=True)
+
+
+def stage_table(cfg, layer, x, topks, gates, routings, reps):
+    """Median microseconds of each stage per imbalance point, caches flushed."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    stages = {
+        "plan": lambda j: layer.plan(topks[j]),
+        "prefetch": lambda j: layer.prefetch(),
+        "dispatch": lambda j: layer.dispatch(x),
+        "gemm": lambda j: layer.gemm_fwd(),
+        "combine": lambda j: layer.combine(gates[j]),
+    }
+    table = {}
+    for j, r in enumerate(routings):
+        layer.plan(topks[j])
+        layer.prefetch()
+        layer.dispatch(x)
+        layer.gemm_fwd()
+        row = {}
+        for name, fn in stages.items():
+            ts = []
+            for _ in range(reps):
+                flush.fill_(1.0)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(j)
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            row[name] = round(float(np.median(ts)), 1)
+        row["replicas"] = int((layer.replica_expert[:, :cfg.B] >= 0).sum())
+        table[f"maxvio={r.maxvio:.3g}"] = row
+    N, K, H, Hp = cfg.N, cfg.K, cfg.H, cfg.Hp
+    plan_b = 12 * N * K + 4 * cfg.R * (cfg.E + cfg.B + 1)
+    disp_b = N * H * 2 + N * K * H * 2 + 4 * N * K
+    comb_b = N * K * Hp * 4 + 8 * N * K + N * Hp * 4
+    t = float(np.mean([v["plan"] + v["dispatch"] + v["combine"] for v in table.values()]))
+    gbs = (plan_b + disp_b + comb_b) / (t * 1e-6) / 1e9
+    hbm = {"bytes": plan_b + disp_b + comb_b, "us": round(t, 1), "achieved": round(gbs, 1),
+           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return table, hbm
+
+
+if __name__ == "__main__":
+    main()

@@ -86,21 +86,37 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
 }
 
 // ------------------------------------------------------------------ staging
-// k-contiguous operand: ROWS x BK tile, row r at base + r*ld; rows >= valid are 0.
+// Operands are read and results written through buffer resources: a 128-bit
+// descriptor (base, byte range) in scalar registers plus a 32-bit offset per
+// lane. Loads past the range return 0 and stores past it are dropped, which
+// zero-fills partial tiles and masks their stores without branches.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;   // raw (unswizzled) 32-bit data, gfx9 family
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used here
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcFlags);
+}
+
+__device__ inline uint32_t clamp_bytes(int64_t b) {
+  return b <= 0 ? 0u : (b >= int64_t(kOffNone) ? kOffNone : uint32_t(b));
+}
+
+// k-contiguous operand: ROWS x BK tile; row r at byte offset r*ld*2 of the
+// descriptor base; rows past the range read as 0.
 template <int ROWS, int BK, int NTHR>
 struct StageK {
   static constexpr int VPR = BK / 8;
   static constexpr int PER = ROWS * VPR / NTHR;
   static_assert(ROWS * VPR % NTHR == 0, "tile must split evenly over the threads");
-  uint4 r[PER];
-  __device__ inline void load(const uint16_t* __restrict__ base, int64_t ld, int rows_valid) {
+  v4i_t r[PER];
+  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, uint32_t ld_bytes) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int v = threadIdx.x + p * NTHR;
       const int row = v / VPR, kv = v % VPR;
-      r[p] = row < rows_valid
-                 ? *reinterpret_cast<const uint4*>(base + int64_t(row) * ld + kv * 8)
-                 : make_uint4(0, 0, 0, 0);
+      r[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * ld_bytes + kv * 16, 0, 0);
     }
   }
   __device__ inline void store(uint16_t* s) const {
@@ -108,52 +124,49 @@ struct StageK {
     for (int p = 0; p < PER; ++p) {
       const int v = threadIdx.x + p * NTHR;
       const int row = v / VPR, kv = v % VPR;
-      *reinterpret_cast<uint4*>(s + row * (BK + 8) + kv * 8) = r[p];
+      *reinterpret_cast<v4i_t*>(s + row * (BK + 8) + kv * 8) = r[p];
     }
   }
 };
 
-// M/N-contiguous operand: BK x COLS tile, k row i at base + i*ld, stored to LDS
-// transposed as [COLS][BK + 8]. Each thread moves KB k-rows x 8 columns per step.
+// M/N-contiguous operand: BK x COLS tile, k row i at byte offset i*ld*2, stored to
+// LDS transposed as [COLS][BK + 8]. Each thread moves KB k-rows x 8 columns per
+// step; consecutive lanes take consecutive k-blocks of one column block, so a
+// store instruction covers whole 16-byte chunks of neighbouring LDS rows (no
+// bank conflicts) while each k row is still read in whole 128-byte lines.
+// Columns at or past cols_valid, and k rows past the range, read as 0.
 template <int COLS, int BK, int NTHR>
 struct StageMN {
   static constexpr int KB0 = BK * COLS / (8 * NTHR);
   static constexpr int KB = KB0 >= 8 ? 8 : KB0;
   static constexpr int STEPS = BK * COLS / (8 * KB * NTHR);
-  static constexpr int CPB = COLS / 8;  // column blocks
+  static constexpr int KPB = BK / KB;   // k blocks per column block
   static_assert(KB == 2 || KB == 4 || KB == 8, "unsupported transposed staging shape");
   static_assert(STEPS * 8 * KB * NTHR == BK * COLS, "tile must split evenly");
-  uint4 r[STEPS][KB];
-  __device__ inline void load(const uint16_t* __restrict__ base, int64_t ld, int k_valid,
-                              int cols_valid) {
+  v4i_t r[STEPS][KB];
+  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, uint32_t ld_bytes, int cols_valid) {
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int mb = threadIdx.x + st * NTHR;
-      const int cb = mb % CPB, kb = mb / CPB;
-      const bool cok = cb * 8 < cols_valid;
+      const int kb = mb % KPB, cb = mb / KPB;
+      const uint32_t base = cb * 8 < cols_valid ? uint32_t(kb * KB) * ld_bytes + cb * 16 : kOffNone;
 #pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const int k = kb * KB + i;
-        r[st][i] = (cok && k < k_valid)
-                       ? *reinterpret_cast<const uint4*>(base + int64_t(k) * ld + cb * 8)
-                       : make_uint4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < KB; ++i)
+        r[st][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + i * ld_bytes, 0, 0);
     }
-  }
-  __device__ static inline uint32_t word(const uint4& v, int d) {
-    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
   }
   __device__ inline void store(uint16_t* s) const {
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int mb = threadIdx.x + st * NTHR;
-      const int cb = mb % CPB, kb = mb / CPB;
+      const int kb = mb % KPB, cb = mb / KPB;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         uint32_t o[KB / 2];
 #pragma unroll
         for (int j = 0; j < KB / 2; ++j) {
-          const uint32_t lo = word(r[st][2 * j], c >> 1), hi = word(r[st][2 * j + 1], c >> 1);
+          const uint32_t lo = uint32_t(r[st][2 * j][c >> 1]);
+          const uint32_t hi = uint32_t(r[st][2 * j + 1][c >> 1]);
           o[j] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
         uint16_t* dst = s + (cb * 8 + c) * (BK + 8) + kb * KB;
@@ -190,14 +203,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   __shared__ __align__(16) uint16_t sA[2][BM * LDK];
   __shared__ __align__(16) uint16_t sB[2][BN * LDK];
 
-  // per-op extents: M x N output tile grid, K reduction
-  const int Mdim_w = g.H;                               // WGRAD M
-  const int Ndim = OP == MOONEP_DGRAD ? g.H : g.Hp;     // N columns of C
-  const int Kfix = OP == MOONEP_FWD ? g.H : g.Hp;       // FWD/DGRAD K
+  const int Ndim = OP == MOONEP_DGRAD ? g.H : g.Hp;   // columns of C
+  const int Kfix = OP == MOONEP_FWD ? g.H : g.Hp;     // FWD/DGRAD reduction length
   const int NT = (Ndim + BN - 1) / BN;
-  const int MT = OP == MOONEP_WGRAD ? (Mdim_w + BM - 1) / BM : 1;
+  const int MT = OP == MOONEP_WGRAD ? (g.H + BM - 1) / BM : 1;
   const int64_t total = int64_t(*g.ntiles) * MT * NT;
   const int64_t wsz = int64_t(g.H) * g.Hp;
+  const uint32_t lda_b = uint32_t(OP == MOONEP_DGRAD ? g.Hp : g.H) * 2;   // bytes per A row
+  const uint32_t ldb_b = uint32_t(g.Hp) * 2;                              // bytes per B row
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -220,27 +233,25 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     int m0, rows_valid, kdim;
     if (OP == MOONEP_WGRAD) {
       m0 = mt * BM;
-      rows_valid = min(BM, Mdim_w - m0);
+      rows_valid = min(BM, g.H - m0);
       kdim = te.n;
     } else {
       m0 = te.m0;
       rows_valid = min(BM, te.n - te.m0);
       kdim = Kfix;
     }
-    // operand base pointers at k = 0 of this tile
+    // operand bases at k = 0 of this tile
     const uint16_t* abase;
-    int64_t lda;
     const uint16_t* bbase;
-    int64_t ldb;
     if (OP == MOONEP_FWD) {
-      abase = g.a + (int64_t(te.rowbase) + m0) * g.H; lda = g.H;
-      bbase = g.b + int64_t(te.wrow) * wsz + n0; ldb = g.Hp;
+      abase = g.a + (int64_t(te.rowbase) + m0) * g.H;
+      bbase = g.b + int64_t(te.wrow) * wsz + n0;
     } else if (OP == MOONEP_DGRAD) {
-      abase = g.a + (int64_t(te.rowbase) + m0) * g.Hp; lda = g.Hp;
-      bbase = g.b + int64_t(te.wrow) * wsz + int64_t(n0) * g.Hp; ldb = g.Hp;
+      abase = g.a + (int64_t(te.rowbase) + m0) * g.Hp;
+      bbase = g.b + int64_t(te.wrow) * wsz + int64_t(n0) * g.Hp;
     } else {
-      abase = g.a + int64_t(te.rowbase) * g.H + m0; lda = g.H;
-      bbase = g.b + int64_t(te.rowbase) * g.Hp + n0; ldb = g.Hp;
+      abase = g.a + int64_t(te.rowbase) * g.H + m0;
+      bbase = g.b + int64_t(te.rowbase) * g.Hp + n0;
     }
 
     floatx16_t acc[FM][FN];
@@ -254,10 +265,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     const int kiters = (kdim + BK - 1) / BK;
     auto load_stage = [&](int kt) {
       const int k0 = kt * BK;
-      if constexpr (A_MN) stA.load(abase + int64_t(k0) * lda, lda, kdim - k0, rows_valid);
-      else stA.load(abase + k0, lda, rows_valid);
-      if constexpr (B_MN) stB.load(bbase + int64_t(k0) * ldb, ldb, kdim - k0, cols_valid);
-      else stB.load(bbase + k0, ldb, cols_valid);
+      if constexpr (A_MN) {
+        stA.load(make_rsrc(abase + int64_t(k0) * g.H, clamp_bytes(int64_t(kdim - k0) * lda_b)),
+                 lda_b, rows_valid);
+      } else {
+        stA.load(make_rsrc(abase + k0, clamp_bytes(int64_t(rows_valid) * lda_b)), lda_b);
+      }
+      if constexpr (B_MN) {
+        stB.load(make_rsrc(bbase + int64_t(k0) * g.Hp, clamp_bytes(int64_t(kdim - k0) * ldb_b)),
+                 ldb_b, cols_valid);
+      } else {
+        stB.load(make_rsrc(bbase + k0, clamp_bytes(int64_t(cols_valid) * ldb_b)), ldb_b);
+      }
     };
 
     if (kiters > 0) {
@@ -269,22 +288,30 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     for (int kt = 0; kt < kiters; ++kt) {
       const int cur = kt & 1;
       if (kt + 1 < kiters) load_stage(kt + 1);
-      const uint16_t* pa = sA[cur];
-      const uint16_t* pb = sB[cur];
+      const uint16_t* pa = sA[cur] + (wm * WM + r32) * LDK + kh;
+      const uint16_t* pb = sB[cur] + (wn * WN + r32) * LDK + kh;
+      // fragments of the next 16-wide k slice are read while this slice's MFMAs run
+      bf16x8_t af[2][FM], bfr[2][FN];
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 16) {
-        bf16x8_t af[FM], bfr[FN];
+      for (int i = 0; i < FM; ++i) af[0][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * LDK);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(pa + (wm * WM + i * 32 + r32) * LDK + kk + kh);
+      for (int j = 0; j < FN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * LDK);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + (wn * WN + j * 32 + r32) * LDK + kk + kh);
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int c = ks & 1;
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            af[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * LDK + (ks + 1) * 16);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            bfr[c ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * LDK + (ks + 1) * 16);
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfr[c][j], acc[i][j], 0, 0, 0);
       }
       if (kt + 1 < kiters) {
         stA.store(sA[cur ^ 1]);
@@ -294,8 +321,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     }
 
     // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
+    // of each 32 x 32 block; rows past rows_valid fall outside the range.
     float* cbase;
-    int64_t ldc;
+    uint32_t ldc;
     if (OP == MOONEP_WGRAD) {
       cbase = (te.wrow < g.E ? g.grad_home + int64_t(te.wrow) * wsz
                              : g.reduce_buf + int64_t(te.wrow - g.E) * wsz) +
@@ -305,20 +333,28 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       cbase = g.c + (int64_t(te.rowbase) + m0) * Ndim + n0;
       ldc = Ndim;
     }
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
+    // per-lane byte offset of each column block (columns past cols_valid fall
+    // outside the range); the row part of the offset is the same for every lane
+    uint32_t lb[FN];
+    const uint32_t lane_row = uint32_t(wm * WM + (lane >> 5) * 4) * ldc * 4;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = wn * WN + j * 32 + r32;
+      lb[j] = col < cols_valid ? lane_row + uint32_t(col) * 4 : kOffNone;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = wn * WN + j * 32 + r32;
-        if (col >= cols_valid) continue;
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * ldc * 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (row < rows_valid) {
-            float* p = cbase + int64_t(row) * ldc + col;
-            if (OP == MOONEP_WGRAD) *p += acc[i][j][r];
-            else *p = acc[i][j][r];
-          }
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t off = lb[j] + rowoff;
+          float v = acc[i][j][r];
+          if (OP == MOONEP_WGRAD)
+            v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, off, 0, 0));
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), crs, off, 0, 0);
         }
       }
   }
@@ -378,14 +414,19 @@ static int device_cus() {
   return cached;
 }
 
-// bf16 tile configuration
-constexpr int kBM = 128, kBN = 128, kBK = 64, kWavesM = 2, kWavesN = 2;
-constexpr int kBlocksPerCU = 2;
+// bf16 tile configuration: 256 x 256 output tile, 4 wavefronts of 128 x 128,
+// k-steps of 64, two LDS stages (147 KB), one workgroup per CU.
+template <int OP>
+struct TileCfg {
+  static constexpr int BM = 256, BN = 256, BK = 64, WAVES_M = 2, WAVES_N = 2;
+};
+constexpr int kBlocksPerCU = 1;
 
 template <int OP>
 static void launch_bf16(const GemmArgs& g, int grid, hipStream_t strm) {
-  gemm_bf16_kernel<OP, kBM, kBN, kBK, kWavesM, kWavesN>
-      <<<grid, kWavesM * kWavesN * 64, 0, strm>>>(g);
+  using C = TileCfg<OP>;
+  gemm_bf16_kernel<OP, C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N>
+      <<<grid, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
 }  // namespace moonep
@@ -402,21 +443,21 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
   if (op != MOONEP_FWD && op != MOONEP_DGRAD && op != MOONEP_WGRAD) return MOONEP_EINVAL;
   if (op != MOONEP_FWD && s.mode != MOONEP_TRAIN) return MOONEP_EMODE;
   if (s.H % 64 || s.Hp % 64) return MOONEP_EINVAL;
-  if (!aligned16(a) || !aligned16(b) || !aligned16(cu_seqlens) || !aligned16(ws))
-    return MOONEP_EINVAL;
+  if (!aligned16(cu_seqlens) || !aligned16(ws)) return MOONEP_EINVAL;
+  const WsLayout w = ws_layout(s);
+  if (ws_bytes < w.total) return MOONEP_EWORKSPACE;
+  if (s.S == 0) return MOONEP_OK;
+  if (!aligned16(a) || !aligned16(b)) return MOONEP_EINVAL;
   if (op == MOONEP_WGRAD) {
     if (!aligned16(grad_home) || (s.B > 0 && !aligned16(reduce_buf))) return MOONEP_EINVAL;
   } else if (!aligned16(c)) {
     return MOONEP_EINVAL;
   }
-  const WsLayout w = ws_layout(s);
-  if (ws_bytes < w.total) return MOONEP_EWORKSPACE;
-  if (s.S == 0) return MOONEP_OK;
   hipStream_t strm = as_stream(stream);
   TileEntry* tiles = ws_ptr<TileEntry>(ws, w.tiles);
   int32_t* ntiles = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount;
   const bool bf16 = s.dtype == MOONEP_BF16;
-  const int bm = (op == MOONEP_WGRAD || !bf16) ? 0 : kBM;
+  const int bm = (op == MOONEP_WGRAD || !bf16) ? 0 : TileCfg<MOONEP_FWD>::BM;
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K, bm, tiles, ntiles,
                                           int(w.max_tiles));
   if (launch_status()) return MOONEP_EHIP;

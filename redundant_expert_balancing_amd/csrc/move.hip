@@ -199,10 +199,10 @@ extern "C" int moonep_dispatch(const moonep_shape* shape, int32_t width, const v
   const moonep_shape& s = *shape;
   const int eb = elem_bytes(s);
   if (width != s.H && width != s.Hp) return MOONEP_EINVAL;
-  if (!aligned16(src) || !aligned16(slot_map) || !aligned16(dst)) return MOONEP_EINVAL;
-  if (gates && !aligned16(gates)) return MOONEP_EINVAL;
   const int N = s.R * s.S;
   if (N == 0) return MOONEP_OK;
+  if (!aligned16(src) || !aligned16(slot_map) || !aligned16(dst)) return MOONEP_EINVAL;
+  if (gates && !aligned16(gates)) return MOONEP_EINVAL;
   const int nvec = width * eb / 16;
   const int64_t ndst = int64_t(N) * s.K;
   const int grid = grid_for(N, 1 << 20);
@@ -243,10 +243,10 @@ extern "C" int moonep_combine(const moonep_shape* shape, int32_t width, const fl
   const moonep_shape& s = *shape;
   if (width != s.H && width != s.Hp) return MOONEP_EINVAL;
   if (width % 4) return MOONEP_EINVAL;
-  if (!aligned16(src) || !aligned16(slot_map) || !aligned16(dst)) return MOONEP_EINVAL;
-  if (gates && !aligned16(gates)) return MOONEP_EINVAL;
   const int N = s.R * s.S;
   if (N == 0) return MOONEP_OK;
+  if (!aligned16(src) || !aligned16(slot_map) || !aligned16(dst)) return MOONEP_EINVAL;
+  if (gates && !aligned16(gates)) return MOONEP_EINVAL;
   const int nvec = width / 4;
   const int grid = grid_for(N, 1 << 20);
   hipStream_t strm = as_stream(stream);

@@ -431,8 +431,10 @@ extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, i
   int st = validate(shape);
   if (st) return st;
   const moonep_shape& s = *shape;
-  if (!aligned16(topk_idx) || !aligned16(cu_seqlens) || !aligned16(slot_map) ||
-      !aligned16(src_index) || !aligned16(ws))
+  const int64_t NK = int64_t(s.R) * s.S * s.K;
+  // arrays with no element to touch (an empty layer) may be NULL
+  if (!aligned16(cu_seqlens) || !aligned16(ws)) return MOONEP_EINVAL;
+  if (NK > 0 && (!aligned16(topk_idx) || !aligned16(slot_map) || !aligned16(src_index)))
     return MOONEP_EINVAL;
   if (s.B > 0 && !aligned16(replica_expert)) return MOONEP_EINVAL;
   const WsLayout w = ws_layout(s);
