@@ -152,3 +152,30 @@ def test_synthetic_layer_inputs_reproducible():
     assert abs(a["W"].float().std().item() - cfg.H ** -0.5) < 0.01
     c = make_dense(CONFIGS["bf16_train_mild"], "cpu", 0, which=("x",))
     assert c["x"].dtype == torch.bfloat16
+
+
+def test_sampled_helpers_against_closed_form_and_autograd():
+    """dense_expert_outputs: rank-one experts give (x.a_e) b_e per slot;
+    wgrad_entries: equals autograd's dW entries for one expert."""
+    rng, topk, gates, x = _tiny_layer(seed=4)
+    E, H, Hp, K = 4, 6, 5, 2
+    a = rng.standard_normal((E, H))
+    b = rng.standard_normal((E, Hp))
+    W = np.einsum("eh,ep->ehp", a, b)
+    out = M.dense_expert_outputs(x, W, topk)
+    for g in range(x.shape[0]):
+        for k in range(K):
+            e = topk[g, k]
+            assert np.allclose(out[g * K + k], float(x[g] @ a[e]) * b[e], rtol=1e-12, atol=1e-12)
+    Wr = rng.standard_normal((E, H, Hp))
+    dy = rng.standard_normal((x.shape[0], Hp)).astype(np.float32)
+    d = M.gated_dy(dy, gates, "fp32")
+    xt = torch.tensor(x, dtype=torch.float64)
+    Wt = torch.tensor(Wr, dtype=torch.float64, requires_grad=True)
+    dt = torch.tensor(d, dtype=torch.float64).view(x.shape[0], K, Hp)
+    (torch.einsum("gh,gkhp->gkp", xt, Wt[torch.from_numpy(topk).long()]) * dt).sum().backward()
+    e = 2
+    tok, kk = np.nonzero(topk == e)
+    hh, pp = np.array([0, 3, 5]), np.array([1, 4])
+    got = M.wgrad_entries(x[tok], d[tok * K + kk], hh, pp)
+    assert np.allclose(got, Wt.grad.numpy()[e][np.ix_(hh, pp)], rtol=1e-12, atol=1e-12)
