@@ -9,12 +9,10 @@
 //   gemm    a persistent kernel walks entry x N-tile (x M-tile for WGRAD) in an
 //           order that keeps the workgroups of one XCD on neighbouring tiles.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, float32 accumulation, operand tiles
-// staged through LDS k-contiguous ([rows][BK + 8], the pad keeps 16-byte
-// fragment reads conflict-free). Operands stored with k contiguous are copied
-// as 16-byte vectors; operands stored with M or N contiguous (the weight in
-// FWD, both operands in WGRAD) are loaded as 16-byte vectors and transposed in
-// registers before the LDS store. Two LDS stages, one barrier per k-step.
+// bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation; operands go
+// global -> LDS by DMA into a ring of k-steps; operands stored with M or N
+// contiguous (the weight in FWD, both operands in WGRAD) stay untransposed in
+// LDS and are read with the gfx950 transposing LDS read.
 // fp32 path: a plain FMA kernel per output element (tiny layers only).
 #include <type_traits>
 
@@ -86,13 +84,25 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
 }
 
 // ------------------------------------------------------------------ staging
-// Operands are read and results written through buffer resources: a 128-bit
+// Operands move global -> LDS by direct DMA (buffer_load_dwordx4 ... lds: lane l
+// of a wavefront writes 16 bytes at M0 + 16*l), through buffer resources: a
 // descriptor (base, byte range) in scalar registers plus a 32-bit offset per
-// lane. Loads past the range return 0 and stores past it are dropped, which
-// zero-fills partial tiles and masks their stores without branches.
+// lane; loads past the range return 0, stores past it are dropped. Partial
+// tiles therefore need no branches. No operand passes through registers, so
+// the k-loop keeps several steps in flight in a ring of LDS stages.
+//
+// LDS layouts of one 32-deep k-step (16-byte chunks XOR-swizzled so that the
+// fragment reads of 8 or 16 lanes at a time hit distinct banks):
+//   k-contiguous operand   [ROWS][32]: 64-byte rows, chunk c of row r at c ^ swz_k(r)
+//   m/n-contiguous operand [32][COLS]: one row per k, chunk c of row k at c ^ swz_mn(k);
+//     read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
+//     column, the MFMA operand layout, without a transpose anywhere else.
 typedef int v4i_t __attribute__((ext_vector_type(4)));
-constexpr int kRsrcFlags = 0x00020000;   // raw (unswizzled) 32-bit data, gfx9 family
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcFlags = 0x00020000;      // raw (unswizzled) 32-bit data, gfx9 family
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used here
+constexpr int kBK = 32;                     // k per pipeline step
+constexpr int kStages = 4;                  // LDS ring depth
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -103,78 +113,105 @@ __device__ inline uint32_t clamp_bytes(int64_t b) {
   return b <= 0 ? 0u : (b >= int64_t(kOffNone) ? kOffNone : uint32_t(b));
 }
 
-// k-contiguous operand: ROWS x BK tile; row r at byte offset r*ld*2 of the
-// descriptor base; rows past the range read as 0.
-template <int ROWS, int BK, int NTHR>
-struct StageK {
-  static constexpr int VPR = BK / 8;
-  static constexpr int PER = ROWS * VPR / NTHR;
-  static_assert(ROWS * VPR % NTHR == 0, "tile must split evenly over the threads");
-  v4i_t r[PER];
-  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, uint32_t ld_bytes) {
+// One 16-byte-per-lane DMA into LDS at byte address lds (uniform). Issued as
+// inline assembly so that the compiler's wait-count pass does not wait for all
+// outstanding DMAs at every LDS read; the k-loop waits for exactly the step it
+// consumes (wait_dma).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Wait until at most n of this wavefront's vector memory operations are pending.
+template <int n>
+__device__ inline void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // s_waitcnt simm16: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and
+  // lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ inline int swz_k(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ inline int swz_mn(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 10 : 0); }
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS byte address of a pointer into __shared__ memory (address-space cast).
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_char*)p));
+}
+
+// k-contiguous operand tile: ROWS rows x 32 k.
+template <int ROWS, int NWAVES>
+struct OpK {
+  static constexpr int BYTES = ROWS * 64;
+  static constexpr int INSTR = BYTES / 1024;  // 16 rows per wavefront DMA
+  static constexpr int PER_WAVE = INSTR / NWAVES;
+  static_assert(INSTR % NWAVES == 0, "DMA split");
+  // rsrc base at (row 0, k0); ld in bytes; rows past the range read 0
+  __device__ static inline void issue(__amdgpu_buffer_rsrc_t rs, uint32_t ld, uint32_t lds,
+                                      int wave, int lane, int /*cols_valid*/) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int v = threadIdx.x + p * NTHR;
-      const int row = v / VPR, kv = v % VPR;
-      r[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * ld_bytes + kv * 16, 0, 0);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int b = wave + i * NWAVES;
+      const int row = b * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_k(row);
+      dma16(rs, uint32_t(row) * ld + c * 16, lds + b * 1024);
     }
   }
-  __device__ inline void store(uint16_t* s) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int v = threadIdx.x + p * NTHR;
-      const int row = v / VPR, kv = v % VPR;
-      *reinterpret_cast<v4i_t*>(s + row * (BK + 8) + kv * 8) = r[p];
-    }
+  // MFMA operand: rows rbase + lane%32, k = 16*ks + 8*(lane/32) .. +8
+  __device__ static inline bf16x8_t frag(const char* st, int rbase, int ks, int lane) {
+    const int row = rbase + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(st + row * 64 + ((c ^ swz_k(row)) << 4));
   }
 };
 
-// M/N-contiguous operand: BK x COLS tile, k row i at byte offset i*ld*2, stored to
-// LDS transposed as [COLS][BK + 8]. Each thread moves KB k-rows x 8 columns per
-// step; consecutive lanes take consecutive k-blocks of one column block, so a
-// store instruction covers whole 16-byte chunks of neighbouring LDS rows (no
-// bank conflicts) while each k row is still read in whole 128-byte lines.
-// Columns at or past cols_valid, and k rows past the range, read as 0.
-template <int COLS, int BK, int NTHR>
-struct StageMN {
-  static constexpr int KB0 = BK * COLS / (8 * NTHR);
-  static constexpr int KB = KB0 >= 8 ? 8 : KB0;
-  static constexpr int STEPS = BK * COLS / (8 * KB * NTHR);
-  static constexpr int KPB = BK / KB;   // k blocks per column block
-  static_assert(KB == 2 || KB == 4 || KB == 8, "unsupported transposed staging shape");
-  static_assert(STEPS * 8 * KB * NTHR == BK * COLS, "tile must split evenly");
-  v4i_t r[STEPS][KB];
-  __device__ inline void load(__amdgpu_buffer_rsrc_t rs, uint32_t ld_bytes, int cols_valid) {
+// m/n-contiguous operand tile: 32 k-rows x COLS.
+template <int COLS, int NWAVES>
+struct OpMN {
+  static constexpr int ROWB = COLS * 2;
+  static constexpr int CPR = ROWB / 16;         // chunks per row
+  static constexpr int BYTES = kBK * ROWB;
+  static constexpr int INSTR = BYTES / 1024;
+  static constexpr int RPI = 1024 / ROWB;       // k rows per wavefront DMA
+  static constexpr int PER_WAVE = INSTR / NWAVES;
+  static_assert(INSTR % NWAVES == 0 && RPI >= 1, "DMA split");
+  // rsrc base at (k0, col 0); ld in bytes; k rows past the range and columns at or
+  // past cols_valid read 0
+  __device__ static inline void issue(__amdgpu_buffer_rsrc_t rs, uint32_t ld, uint32_t lds,
+                                      int wave, int lane, int cols_valid) {
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int mb = threadIdx.x + st * NTHR;
-      const int kb = mb % KPB, cb = mb / KPB;
-      const uint32_t base = cb * 8 < cols_valid ? uint32_t(kb * KB) * ld_bytes + cb * 16 : kOffNone;
-#pragma unroll
-      for (int i = 0; i < KB; ++i)
-        r[st][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + i * ld_bytes, 0, 0);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int b = wave + i * NWAVES;
+      const int k = b * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz_mn(k);
+      const uint32_t off = c * 8 < cols_valid ? uint32_t(k) * ld + c * 16 : kOffNone;
+      dma16(rs, off, lds + b * 1024);
     }
   }
-  __device__ inline void store(uint16_t* s) const {
+  // MFMA operand: column cbase + lane%32, k = 16*ks + 8*(lane/32) .. +8, as two
+  // transposed 4x16 reads per 16-lane group
+  __device__ static inline bf16x8_t frag(const char* st, int cbase, int ks, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int col = cbase + 16 * (g & 1) + 4 * (i & 3);
+    const int c = col >> 3, half = (col >> 2) & 1;
+    const int k0 = ks * 16 + (g >> 1) * 8 + (i >> 2);
+    v4s_t v[2];
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      const int mb = threadIdx.x + st * NTHR;
-      const int kb = mb % KPB, cb = mb / KPB;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint32_t o[KB / 2];
-#pragma unroll
-        for (int j = 0; j < KB / 2; ++j) {
-          const uint32_t lo = uint32_t(r[st][2 * j][c >> 1]);
-          const uint32_t hi = uint32_t(r[st][2 * j + 1][c >> 1]);
-          o[j] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-        }
-        uint16_t* dst = s + (cb * 8 + c) * (BK + 8) + kb * KB;
-        if constexpr (KB == 2) *reinterpret_cast<uint32_t*>(dst) = o[0];
-        else if constexpr (KB == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
-        else *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 4 * h;
+      const char* p = st + k * ROWB + ((c ^ swz_mn(k)) << 4) + half * 8;
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)((const lds_char*)p));
     }
+    const v4i_t w = {int((uint16_t)v[0][0] | ((uint32_t)(uint16_t)v[0][1] << 16)),
+                     int((uint16_t)v[0][2] | ((uint32_t)(uint16_t)v[0][3] << 16)),
+                     int((uint16_t)v[1][0] | ((uint32_t)(uint16_t)v[1][1] << 16)),
+                     int((uint16_t)v[1][2] | ((uint32_t)(uint16_t)v[1][3] << 16))};
+    return __builtin_bit_cast(bf16x8_t, w);
   }
 };
 
@@ -190,18 +227,18 @@ struct GemmArgs {
   int H, Hp, E;
 };
 
-template <int OP, int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+template <int OP, int BM, int BN, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NTHR = WAVES_M * WAVES_N * 64;
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int LDK = BK + 8;
-  static_assert(FM >= 1 && FN >= 1 && BK % 16 == 0, "tile shape");
-  constexpr bool A_MN = OP == MOONEP_WGRAD;  // A stored m-contiguous
-  constexpr bool B_MN = OP != MOONEP_DGRAD;  // B stored n-contiguous
-
-  __shared__ __align__(16) uint16_t sA[2][BM * LDK];
-  __shared__ __align__(16) uint16_t sB[2][BN * LDK];
+  static_assert(FM >= 1 && FN >= 1, "tile shape");
+  // A stored k-contiguous except in WGRAD; B stored n-contiguous except in DGRAD
+  using OA = typename std::conditional<OP == MOONEP_WGRAD, OpMN<BM, NW>, OpK<BM, NW>>::type;
+  using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, NW>, OpMN<BN, NW>>::type;
+  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int DMA_PER_STEP = OA::PER_WAVE + OB::PER_WAVE;
+  __shared__ __align__(1024) char smem[kStages * STAGE];
 
   const int Ndim = OP == MOONEP_DGRAD ? g.H : g.Hp;   // columns of C
   const int Kfix = OP == MOONEP_FWD ? g.H : g.Hp;     // FWD/DGRAD reduction length
@@ -214,14 +251,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
-  const int r32 = lane & 31, kh = (lane >> 5) * 8;
+  const uint32_t lds0 = lds_addr(smem);
 
   // XCD-aware order: the workgroups of one XCD take a contiguous run of tiles.
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-
-  typename std::conditional<A_MN, StageMN<BM, BK, NTHR>, StageK<BM, BK, NTHR>>::type stA;
-  typename std::conditional<B_MN, StageMN<BN, BK, NTHR>, StageK<BN, BK, NTHR>>::type stB;
 
   for (int64_t tau = slot; tau < total; tau += G) {
     const int64_t ent = tau / (int64_t(MT) * NT);
@@ -240,19 +274,33 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       rows_valid = min(BM, te.n - te.m0);
       kdim = Kfix;
     }
-    // operand bases at k = 0 of this tile
-    const uint16_t* abase;
-    const uint16_t* bbase;
-    if (OP == MOONEP_FWD) {
-      abase = g.a + (int64_t(te.rowbase) + m0) * g.H;
-      bbase = g.b + int64_t(te.wrow) * wsz + n0;
-    } else if (OP == MOONEP_DGRAD) {
-      abase = g.a + (int64_t(te.rowbase) + m0) * g.Hp;
-      bbase = g.b + int64_t(te.wrow) * wsz + int64_t(n0) * g.Hp;
-    } else {
-      abase = g.a + int64_t(te.rowbase) * g.H + m0;
-      bbase = g.b + int64_t(te.rowbase) * g.Hp + n0;
-    }
+    const int kiters = (kdim + kBK - 1) / kBK;
+
+    // issue the DMAs of k-step kt into ring stage kt % kStages
+    auto issue = [&](int kt) {
+      const int k0 = kt * kBK;
+      const uint32_t st = lds0 + uint32_t(kt % kStages) * STAGE;
+      if constexpr (OP == MOONEP_FWD) {
+        OA::issue(make_rsrc(g.a + (int64_t(te.rowbase) + m0) * g.H + k0,
+                            clamp_bytes(int64_t(rows_valid) * lda_b)), lda_b, st, wid, lane, 0);
+        OB::issue(make_rsrc(g.b + int64_t(te.wrow) * wsz + int64_t(k0) * g.Hp + n0,
+                            clamp_bytes(int64_t(kdim - k0) * ldb_b)), ldb_b, st + OA::BYTES,
+                  wid, lane, cols_valid);
+      } else if constexpr (OP == MOONEP_DGRAD) {
+        OA::issue(make_rsrc(g.a + (int64_t(te.rowbase) + m0) * g.Hp + k0,
+                            clamp_bytes(int64_t(rows_valid) * lda_b)), lda_b, st, wid, lane, 0);
+        OB::issue(make_rsrc(g.b + int64_t(te.wrow) * wsz + int64_t(n0) * g.Hp + k0,
+                            clamp_bytes(int64_t(cols_valid) * ldb_b)), ldb_b, st + OA::BYTES,
+                  wid, lane, 0);
+      } else {
+        OA::issue(make_rsrc(g.a + (int64_t(te.rowbase) + k0) * g.H + m0,
+                            clamp_bytes(int64_t(kdim - k0) * lda_b)), lda_b, st, wid, lane,
+                  rows_valid);
+        OB::issue(make_rsrc(g.b + (int64_t(te.rowbase) + k0) * g.Hp + n0,
+                            clamp_bytes(int64_t(kdim - k0) * ldb_b)), ldb_b, st + OA::BYTES,
+                  wid, lane, cols_valid);
+      }
+    };
 
     floatx16_t acc[FM][FN];
 #pragma unroll
@@ -262,62 +310,35 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int kiters = (kdim + BK - 1) / BK;
-    auto load_stage = [&](int kt) {
-      const int k0 = kt * BK;
-      if constexpr (A_MN) {
-        stA.load(make_rsrc(abase + int64_t(k0) * g.H, clamp_bytes(int64_t(kdim - k0) * lda_b)),
-                 lda_b, rows_valid);
-      } else {
-        stA.load(make_rsrc(abase + k0, clamp_bytes(int64_t(rows_valid) * lda_b)), lda_b);
-      }
-      if constexpr (B_MN) {
-        stB.load(make_rsrc(bbase + int64_t(k0) * g.Hp, clamp_bytes(int64_t(kdim - k0) * ldb_b)),
-                 ldb_b, cols_valid);
-      } else {
-        stB.load(make_rsrc(bbase + k0, clamp_bytes(int64_t(cols_valid) * ldb_b)), ldb_b);
-      }
-    };
-
-    if (kiters > 0) {
-      load_stage(0);
-      stA.store(sA[0]);
-      stB.store(sB[0]);
-    }
+    // every wavefront has finished reading the ring (previous tile) before refilling it
     __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+      if (p < kiters) issue(p);
+
     for (int kt = 0; kt < kiters; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < kiters) load_stage(kt + 1);
-      const uint16_t* pa = sA[cur] + (wm * WM + r32) * LDK + kh;
-      const uint16_t* pb = sB[cur] + (wn * WN + r32) * LDK + kh;
-      // fragments of the next 16-wide k slice are read while this slice's MFMAs run
-      bf16x8_t af[2][FM], bfr[2][FN];
+      // steps issued after kt that may stay in flight: min(kStages - 2, kiters - 1 - kt)
+      const int ahead = min(kStages - 2, kiters - 1 - kt);
+      if (ahead >= 2) wait_vm<2 * DMA_PER_STEP>();
+      else if (ahead == 1) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
+      __syncthreads();
+      // the stage refilled here was last read in step kt-1, finished by everyone
+      if (kt + kStages - 1 < kiters) issue(kt + kStages - 1);
+      const char* st = smem + (kt % kStages) * STAGE;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[0][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * LDK);
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * LDK);
+        for (int i = 0; i < FM; ++i) af[i] = OA::frag(st, wm * WM + i * 32, ks, lane);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int c = ks & 1;
-        if (ks + 1 < BK / 16) {
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            af[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * LDK + (ks + 1) * 16);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bfr[c ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * LDK + (ks + 1) * 16);
-        }
+        for (int j = 0; j < FN; ++j) bfr[j] = OB::frag(st + OA::BYTES, wn * WN + j * 32, ks, lane);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfr[c][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < kiters) {
-        stA.store(sA[cur ^ 1]);
-        stB.store(sB[cur ^ 1]);
-      }
-      __syncthreads();
     }
 
     // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
@@ -334,8 +355,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       ldc = Ndim;
     }
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
-    // per-lane byte offset of each column block (columns past cols_valid fall
-    // outside the range); the row part of the offset is the same for every lane
+    const int r32 = lane & 31;
     uint32_t lb[FN];
     const uint32_t lane_row = uint32_t(wm * WM + (lane >> 5) * 4) * ldc * 4;
 #pragma unroll
@@ -414,19 +434,18 @@ static int device_cus() {
   return cached;
 }
 
-// bf16 tile configuration: 256 x 256 output tile, 4 wavefronts of 128 x 128,
-// k-steps of 64, two LDS stages (147 KB), one workgroup per CU.
+// bf16 tile configuration: 256 x 256 output tiles, 4 wavefronts of 128 x 128,
+// 32-deep k-steps in a 4-stage LDS ring (128 KiB), one workgroup per CU.
 template <int OP>
 struct TileCfg {
-  static constexpr int BM = 256, BN = 256, BK = 64, WAVES_M = 2, WAVES_N = 2;
+  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 2, PER_CU = 1;
 };
-constexpr int kBlocksPerCU = 1;
 
 template <int OP>
-static void launch_bf16(const GemmArgs& g, int grid, hipStream_t strm) {
+static void launch_bf16(const GemmArgs& g, int cus, hipStream_t strm) {
   using C = TileCfg<OP>;
-  gemm_bf16_kernel<OP, C::BM, C::BN, C::BK, C::WAVES_M, C::WAVES_N>
-      <<<grid, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
+  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N>
+      <<<cus * C::PER_CU, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
 }  // namespace moonep
@@ -467,10 +486,9 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
     if (cus <= 0) return MOONEP_EHIP;
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
                reduce_buf, tiles, ntiles, s.H, s.Hp, s.E};
-    const int grid = cus * kBlocksPerCU;
-    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, grid, strm);
-    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, grid, strm);
-    else launch_bf16<MOONEP_WGRAD>(g, grid, strm);
+    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, cus, strm);
+    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, cus, strm);
+    else launch_bf16<MOONEP_WGRAD>(g, cus, strm);
   } else {
     const dim3 grid(64, 256);
     const float* af = static_cast<const float*>(a);
