@@ -319,7 +319,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     for (int kt = 0; kt < kiters; ++kt) {
       // steps issued after kt that may stay in flight: min(kStages - 2, kiters - 1 - kt)
       const int ahead = min(kStages - 2, kiters - 1 - kt);
-      if (ahead >= 2) wait_vm<2 * DMA_PER_STEP>();
+      if (ahead >= 3) wait_vm<3 * DMA_PER_STEP>();
+      else if (ahead == 2) wait_vm<2 * DMA_PER_STEP>();
       else if (ahead == 1) wait_vm<DMA_PER_STEP>();
       else wait_vm<0>();
       __syncthreads();
@@ -434,11 +435,12 @@ static int device_cus() {
   return cached;
 }
 
-// bf16 tile configuration: 256 x 256 output tiles, 4 wavefronts of 128 x 128,
+// bf16 tile configuration: 256 x 256 output tiles, 8 wavefronts (two per SIMD, so
+// one wavefront's LDS reads and waits overlap the other's MFMAs) of 128 x 64,
 // 32-deep k-steps in a 4-stage LDS ring (128 KiB), one workgroup per CU.
 template <int OP>
 struct TileCfg {
-  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 2, PER_CU = 1;
+  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, PER_CU = 1;
 };
 
 template <int OP>
