@@ -43,26 +43,49 @@ __device__ inline uint4 scale_vec(uint4 v, float g, bool bf16) {
   return v;
 }
 
-// One workgroup per token: read the row once, write it to its K destinations.
-template <bool GATED, bool BF16>
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+__device__ inline v4u_t scale_v4u(v4u_t v, float g, bool bf16) {
+  uint4 u = make_uint4(v.x, v.y, v.z, v.w);
+  u = scale_vec(u, g, bf16);
+  return v4u_t{u.x, u.y, u.z, u.w};
+}
+
+// One workgroup per token: each thread loads up to VPT 16-byte vectors of the
+// row first, then writes them to the K destinations (plain stores: measured
+// faster than non-temporal ones for this write-heavy scatter).
+template <bool GATED, bool BF16, int VPT>
 __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
-    const uint4* __restrict__ src, int nvec, int N, int K, const int32_t* __restrict__ slot_map,
-    const float* __restrict__ gates, uint4* __restrict__ dst, int64_t ndst) {
+    const v4u_t* __restrict__ src, int nvec, int N, int K, const int32_t* __restrict__ slot_map,
+    const float* __restrict__ gates, v4u_t* __restrict__ dst, int64_t ndst) {
   __shared__ int32_t s_slot[kMaxK];
   __shared__ float s_gate[kMaxK];
   for (int g = blockIdx.x; g < N; g += gridDim.x) {
     if (threadIdx.x < K) {
-      s_slot[threadIdx.x] = slot_map[int64_t(g) * K + threadIdx.x];
+      const int d = slot_map[int64_t(g) * K + threadIdx.x];
+      s_slot[threadIdx.x] = (d >= 0 && d < ndst) ? d : -1;
       if (GATED) s_gate[threadIdx.x] = gates[int64_t(g) * K + threadIdx.x];
     }
     __syncthreads();
-    const uint4* row = src + int64_t(g) * nvec;
-    for (int v = threadIdx.x; v < nvec; v += kMoveThreads) {
-      const uint4 val = row[v];
+    const v4u_t* row = src + int64_t(g) * nvec;
+    for (int v0 = 0; v0 < nvec; v0 += VPT * kMoveThreads) {
+      v4u_t val[VPT];
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int v = v0 + i * kMoveThreads + threadIdx.x;
+        if (v < nvec) val[i] = row[v];
+      }
       for (int k = 0; k < K; ++k) {
         const int d = s_slot[k];
-        if (d < 0 || d >= ndst) continue;
-        dst[int64_t(d) * nvec + v] = GATED ? scale_vec(val, s_gate[k], BF16) : val;
+        if (d < 0) continue;
+        v4u_t* out = dst + int64_t(d) * nvec;
+        const float gk = GATED ? s_gate[k] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+          const int v = v0 + i * kMoveThreads + threadIdx.x;
+          if (v < nvec) out[v] = GATED ? scale_v4u(val[i], gk, BF16) : val[i];
+        }
       }
     }
     __syncthreads();
@@ -70,10 +93,12 @@ __global__ __launch_bounds__(kMoveThreads) void dispatch_kernel(
 }
 
 // One workgroup per token: y[g] = sum over k ascending of w_k * src[slot(g,k)].
-template <bool GATED, int KC>  // KC > 0: K known at compile time
+// Each thread issues all K x VPT loads before the multiply-adds; the expert
+// outputs are read exactly once, so the loads are non-temporal.
+template <bool GATED, int KC, int VPT>  // KC > 0: K known at compile time
 __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
-    const float4* __restrict__ src, int nvec, int N, int Kr, const int32_t* __restrict__ slot_map,
-    const float* __restrict__ gates, float4* __restrict__ dst, int64_t nsrc) {
+    const v4f_t* __restrict__ src, int nvec, int N, int Kr, const int32_t* __restrict__ slot_map,
+    const float* __restrict__ gates, v4f_t* __restrict__ dst, int64_t nsrc) {
   __shared__ int32_t s_slot[kMaxK];
   __shared__ float s_gate[kMaxK];
   const int K = KC > 0 ? KC : Kr;
@@ -84,32 +109,52 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
       s_gate[threadIdx.x] = GATED ? gates[int64_t(g) * K + threadIdx.x] : 1.0f;
     }
     __syncthreads();
-    for (int v = threadIdx.x; v < nvec; v += kMoveThreads) {
-      float4 x[KC > 0 ? KC : 1];
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (KC > 0) {
+    for (int v0 = 0; v0 < nvec; v0 += VPT * kMoveThreads) {
+      v4f_t acc[VPT];
 #pragma unroll
-        for (int k = 0; k < (KC > 0 ? KC : 1); ++k) {
+      for (int i = 0; i < VPT; ++i) acc[i] = v4f_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KC > 0) {
+        v4f_t x[KC][VPT];
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
           const int d = s_slot[k];
-          x[k] = d >= 0 ? src[int64_t(d) * nvec + v] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * kMoveThreads + threadIdx.x;
+            x[k][i] = (d >= 0 && v < nvec) ? __builtin_nontemporal_load(src + int64_t(d) * nvec + v)
+                                           : v4f_t{0.f, 0.f, 0.f, 0.f};
+          }
         }
 #pragma unroll
-        for (int k = 0; k < (KC > 0 ? KC : 1); ++k) {
+        for (int k = 0; k < KC; ++k) {
           const float w = s_gate[k];
-          acc.x = fmaf(w, x[k].x, acc.x); acc.y = fmaf(w, x[k].y, acc.y);
-          acc.z = fmaf(w, x[k].z, acc.z); acc.w = fmaf(w, x[k].w, acc.w);
+#pragma unroll
+          for (int i = 0; i < VPT; ++i) {
+            acc[i].x = fmaf(w, x[k][i].x, acc[i].x); acc[i].y = fmaf(w, x[k][i].y, acc[i].y);
+            acc[i].z = fmaf(w, x[k][i].z, acc[i].z); acc[i].w = fmaf(w, x[k][i].w, acc[i].w);
+          }
         }
       } else {
         for (int k = 0; k < K; ++k) {
           const int d = s_slot[k];
           if (d < 0) continue;
-          const float4 y = src[int64_t(d) * nvec + v];
           const float w = s_gate[k];
-          acc.x = fmaf(w, y.x, acc.x); acc.y = fmaf(w, y.y, acc.y);
-          acc.z = fmaf(w, y.z, acc.z); acc.w = fmaf(w, y.w, acc.w);
+#pragma unroll
+          for (int i = 0; i < VPT; ++i) {
+            const int v = v0 + i * kMoveThreads + threadIdx.x;
+            if (v < nvec) {
+              const v4f_t y = __builtin_nontemporal_load(src + int64_t(d) * nvec + v);
+              acc[i].x = fmaf(w, y.x, acc[i].x); acc[i].y = fmaf(w, y.y, acc[i].y);
+              acc[i].z = fmaf(w, y.z, acc[i].z); acc[i].w = fmaf(w, y.w, acc[i].w);
+            }
+          }
         }
       }
-      dst[int64_t(g) * nvec + v] = acc;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int v = v0 + i * kMoveThreads + threadIdx.x;
+        if (v < nvec) dst[int64_t(g) * nvec + v] = acc[i];
+      }
     }
     __syncthreads();
   }
@@ -207,32 +252,45 @@ extern "C" int moonep_dispatch(const moonep_shape* shape, int32_t width, const v
   const int64_t ndst = int64_t(N) * s.K;
   const int grid = grid_for(N, 1 << 20);
   hipStream_t strm = as_stream(stream);
-  const uint4* sv = static_cast<const uint4*>(src);
-  uint4* dv = static_cast<uint4*>(dst);
-  if (!gates)
-    dispatch_kernel<false, true><<<grid, kMoveThreads, 0, strm>>>(sv, nvec, N, s.K, slot_map,
-                                                                 nullptr, dv, ndst);
-  else if (s.dtype == MOONEP_BF16)
-    dispatch_kernel<true, true><<<grid, kMoveThreads, 0, strm>>>(sv, nvec, N, s.K, slot_map,
-                                                                gates, dv, ndst);
-  else
-    dispatch_kernel<true, false><<<grid, kMoveThreads, 0, strm>>>(sv, nvec, N, s.K, slot_map,
-                                                                 gates, dv, ndst);
+  const v4u_t* sv = static_cast<const v4u_t*>(src);
+  v4u_t* dv = static_cast<v4u_t*>(dst);
+  // vectors per thread: enough that one pass covers the row when it is short
+  const int vpt = nvec <= kMoveThreads ? 1 : nvec <= 2 * kMoveThreads ? 2 : 4;
+#define MOONEP_DISPATCH(G, B, V) \
+  dispatch_kernel<G, B, V><<<grid, kMoveThreads, 0, strm>>>(sv, nvec, N, s.K, slot_map, gates, dv, ndst)
+  const bool bf = s.dtype == MOONEP_BF16;
+  if (!gates) {
+    if (vpt == 1) MOONEP_DISPATCH(false, true, 1);
+    else if (vpt == 2) MOONEP_DISPATCH(false, true, 2);
+    else MOONEP_DISPATCH(false, true, 4);
+  } else if (bf) {
+    if (vpt == 1) MOONEP_DISPATCH(true, true, 1);
+    else if (vpt == 2) MOONEP_DISPATCH(true, true, 2);
+    else MOONEP_DISPATCH(true, true, 4);
+  } else {
+    if (vpt == 1) MOONEP_DISPATCH(true, false, 1);
+    else if (vpt == 2) MOONEP_DISPATCH(true, false, 2);
+    else MOONEP_DISPATCH(true, false, 4);
+  }
+#undef MOONEP_DISPATCH
   return launch_status();
 }
 
-template <bool GATED>
-static void launch_combine(int grid, hipStream_t strm, const float4* src, int nvec, int N, int K,
-                           const int32_t* slot_map, const float* gates, float4* dst,
+template <bool GATED, int VPT>
+static void launch_combine(int grid, hipStream_t strm, const v4f_t* src, int nvec, int N, int K,
+                           const int32_t* slot_map, const float* gates, v4f_t* dst,
                            int64_t nsrc) {
+#define MOONEP_COMBINE(KC) \
+  combine_kernel<GATED, KC, VPT><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc)
   switch (K) {
-    case 1: combine_kernel<GATED, 1><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc); break;
-    case 2: combine_kernel<GATED, 2><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc); break;
-    case 4: combine_kernel<GATED, 4><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc); break;
-    case 6: combine_kernel<GATED, 6><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc); break;
-    case 8: combine_kernel<GATED, 8><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc); break;
-    default: combine_kernel<GATED, 0><<<grid, kMoveThreads, 0, strm>>>(src, nvec, N, K, slot_map, gates, dst, nsrc); break;
+    case 1: MOONEP_COMBINE(1); break;
+    case 2: MOONEP_COMBINE(2); break;
+    case 4: MOONEP_COMBINE(4); break;
+    case 6: MOONEP_COMBINE(6); break;
+    case 8: MOONEP_COMBINE(8); break;
+    default: MOONEP_COMBINE(0); break;
   }
+#undef MOONEP_COMBINE
 }
 
 extern "C" int moonep_combine(const moonep_shape* shape, int32_t width, const float* src,
@@ -250,13 +308,17 @@ extern "C" int moonep_combine(const moonep_shape* shape, int32_t width, const fl
   const int nvec = width / 4;
   const int grid = grid_for(N, 1 << 20);
   hipStream_t strm = as_stream(stream);
-  const float4* sv = reinterpret_cast<const float4*>(src);
-  float4* dv = reinterpret_cast<float4*>(dst);
+  const v4f_t* sv = reinterpret_cast<const v4f_t*>(src);
+  v4f_t* dv = reinterpret_cast<v4f_t*>(dst);
   const int64_t nsrc = int64_t(N) * s.K;
-  if (gates)
-    launch_combine<true>(grid, strm, sv, nvec, N, s.K, slot_map, gates, dv, nsrc);
-  else
-    launch_combine<false>(grid, strm, sv, nvec, N, s.K, slot_map, nullptr, dv, nsrc);
+  const bool two = nvec > kMoveThreads;   // two vectors per thread for long rows
+  if (gates) {
+    if (two) launch_combine<true, 2>(grid, strm, sv, nvec, N, s.K, slot_map, gates, dv, nsrc);
+    else launch_combine<true, 1>(grid, strm, sv, nvec, N, s.K, slot_map, gates, dv, nsrc);
+  } else {
+    if (two) launch_combine<false, 2>(grid, strm, sv, nvec, N, s.K, slot_map, nullptr, dv, nsrc);
+    else launch_combine<false, 1>(grid, strm, sv, nvec, N, s.K, slot_map, nullptr, dv, nsrc);
+  }
   return launch_status();
 }
 
