@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--table", action="store_true",
+                    help="only print per-stage microseconds for every layer configuration")
     return ap.parse_args()
 
 
@@ -135,6 +137,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.table:
+        all_configs_table(args.stage_reps)
         return
     L.lib()   # fail loudly if the HIP library is missing
 
@@ -267,6 +272,63 @@ def stage_table(cfg, layer, x, topks, gates, routings, reps):
     hbm = {"bytes": plan_b + disp_b + comb_b, "us": round(t, 1), "achieved": round(gbs, 1),
            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     return table, hbm
+
+
+def all_configs_table(reps):
+    """Median microseconds per stage (caches flushed before each repetition) for
+    every layer configuration and imbalance point; backward stages where the
+    layer trains with backward."""
+    import numpy as np
+    import torch
+
+    from redundant_expert_balancing_amd.layer import MoEProjection
+    from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return round(float(np.median(ts)), 1)
+
+    out = {}
+    for name, cfg in CONFIGS.items():
+        d = make_dense(cfg, "cuda", 0, which=("x", "W", "dy") if cfg.backward else ("x", "W"),
+                       w_rows=cfg.E + cfg.R * cfg.B)
+        layer = MoEProjection(cfg, "cuda", backward=cfg.backward, w_all=d["W"])
+        for target in cfg.maxvio:
+            r = make_routing(cfg, target)
+            topk = torch.from_numpy(r.topk_idx).cuda()
+            gates = torch.from_numpy(r.gates).cuda()
+            layer.forward(topk, d["x"], gates)
+            row = {"plan": timed(lambda: layer.plan(topk)),
+                   "prefetch": timed(layer.prefetch),
+                   "dispatch": timed(lambda: layer.dispatch(d["x"])),
+                   "gemm": timed(layer.gemm_fwd),
+                   "combine": timed(lambda: layer.combine(gates))}
+            if cfg.backward:
+                from redundant_expert_balancing_amd import _lib as L
+                sh = layer.shape
+                row["dispatch_dy"] = timed(lambda: L.moonep_dispatch(sh, cfg.Hp, d["dy"], layer.slot_map, gates, layer.dyp))
+                row["dgrad"] = timed(lambda: L.moonep_grouped_gemm(sh, L.DGRAD, layer.dyp, layer.w_all, layer.cu_seqlens, layer.dxp, None, None, layer.ws))
+                row["wgrad"] = timed(lambda: L.moonep_grouped_gemm(sh, L.WGRAD, layer.xp, layer.dyp, layer.cu_seqlens, None, layer.grad_home, layer.reduce_buf, layer.ws))
+                row["unpermute"] = timed(lambda: L.moonep_combine(sh, cfg.H, layer.dxp, layer.slot_map, None, layer.dx))
+                row["reduce_grad"] = timed(lambda: L.moonep_reduce_grad(sh, layer.replica_expert, layer.reduce_buf, layer.grad_home))
+            row["replicas"] = int((layer.replica_expert[:, :cfg.B] >= 0).sum()) if cfg.B else 0
+            out[f"{name} maxvio={r.maxvio:.3g}"] = row
+            print(f"[table] {name} {target}: {row}", file=sys.stderr, flush=True)
+        del layer, d
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -207,3 +207,44 @@ def test_backward_full_size_sampled():
 def test_backward_small_full_compare(dtype):
     cfg = small_cfg(name=f"bwd_small_{dtype}", R=4, S=96, E=16, K=4, H=128, Hp=192, dtype=dtype)
     _backward_check(cfg, 3.0, alpha=2.5, full=True)
+
+
+def test_whole_layer_graph_capture_replays_match_eager():
+    """Forward + backward captured in one HIP graph; three replays, each after
+    eager work and a reset of the += gradient targets, equal the eager run bit
+    for bit (the path is deterministic and never synchronises with the host)."""
+    cfg = small_cfg(name="graph", R=4, S=96, E=16, K=4, H=128, Hp=192)
+    say("graph capture", cfg.name)
+    r, layer, d, topk, gates = _setup(cfg, 3.0, backward=True, alpha=2.5)
+
+    def run():
+        layer.forward(topk, d["x"], gates)
+        layer.backward(d["dy"], gates)
+
+    layer.grad_home.zero_()
+    run()
+    torch.cuda.synchronize()
+    want = {k: getattr(layer, k).clone() for k in ("y", "dx", "grad_home", "cu_seqlens", "slot_map")}
+    assert int(torch.count_nonzero(layer.reduce_buf)) == 0
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.grad_home.zero_()
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        layer.grad_home.zero_()
+        layer.y.fill_(float("nan"))
+        layer.dx.fill_(float("nan"))
+        layer.slot_map.fill_(-5)
+        _ = (torch.randn(4096, device="cuda") @ torch.randn(4096, 64, device="cuda")).sum().item()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in want.items():
+            assert torch.equal(getattr(layer, k), v), (rep, k)
+        assert int(torch.count_nonzero(layer.reduce_buf)) == 0
