@@ -249,7 +249,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   const uint32_t lda_b = uint32_t(OP == MOONEP_DGRAD ? g.Hp : g.H) * 2;   // bytes per A row
   const uint32_t ldb_b = uint32_t(g.Hp) * 2;                              // bytes per B row
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // the wavefront id is uniform: keep it (and every LDS address derived from it)
+  // in scalar registers
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const uint32_t lds0 = lds_addr(smem);
 
@@ -316,16 +319,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     for (int p = 0; p < kStages - 1; ++p)
       if (p < kiters) issue(p);
 
-    for (int kt = 0; kt < kiters; ++kt) {
-      // steps issued after kt that may stay in flight: min(kStages - 2, kiters - 1 - kt)
-      const int ahead = min(kStages - 2, kiters - 1 - kt);
-      if (ahead >= 3) wait_vm<3 * DMA_PER_STEP>();
-      else if (ahead == 2) wait_vm<2 * DMA_PER_STEP>();
-      else if (ahead == 1) wait_vm<DMA_PER_STEP>();
-      else wait_vm<0>();
-      __syncthreads();
-      // the stage refilled here was last read in step kt-1, finished by everyone
-      if (kt + kStages - 1 < kiters) issue(kt + kStages - 1);
+    auto compute = [&](int kt) {
       const char* st = smem + (kt % kStages) * STAGE;
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
@@ -340,6 +334,24 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
+    };
+    // steady state: kStages-2 later steps stay in flight while step kt is consumed
+    int kt = 0;
+    for (; kt + kStages - 2 < kiters; ++kt) {
+      wait_vm<(kStages - 2) * DMA_PER_STEP>();
+      __syncthreads();
+      // the stage refilled here was last read in step kt-1, finished by everyone
+      if (kt + kStages - 1 < kiters) issue(kt + kStages - 1);
+      compute(kt);
+    }
+    // tail: fewer steps in flight
+    for (; kt < kiters; ++kt) {
+      const int ahead = kiters - 1 - kt;   // < kStages - 2
+      if (ahead >= 2) wait_vm<2 * DMA_PER_STEP>();
+      else if (ahead == 1) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
+      __syncthreads();
+      compute(kt);
     }
 
     // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
