@@ -48,6 +48,8 @@ def parse():
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--table", action="store_true",
                     help="only print per-stage microseconds for every layer configuration")
+    ap.add_argument("--home-only-baseline", action="store_true",
+                    help="only print per-rank grouped-GEMM time, balanced vs plain EP")
     return ap.parse_args()
 
 
@@ -140,6 +142,9 @@ def main():
         return
     if args.table:
         all_configs_table(args.stage_reps)
+        return
+    if args.home_only_baseline:
+        home_only_baseline(args.stage_reps)
         return
     L.lib()   # fail loudly if the HIP library is missing
 
@@ -327,6 +332,68 @@ def all_configs_table(reps):
             out[f"{name} maxvio={r.maxvio:.3g}"] = row
             print(f"[table] {name} {target}: {row}", file=sys.stderr, flush=True)
         del layer, d
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
+def home_only_baseline(reps):
+    """Per-rank grouped-GEMM time at the bench shape, as if every rank ran on its
+    own GPU: the balanced plan (S*K rows per rank) against plain EP without
+    redundant experts (rank q computes all L_q rows of its home experts). The
+    layer waits for the slowest rank, so the max over ranks is the layer time."""
+    import numpy as np
+    import torch
+
+    from redundant_expert_balancing_amd.baseline import balanced_rank, home_only_ranks
+    from redundant_expert_balancing_amd.layer import MoEProjection
+    from redundant_expert_balancing_amd.synth import CONFIGS, LayerConfig, make_dense, make_routing
+
+    cfg = CONFIGS["bench_shape"]
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    d = make_dense(cfg, "cuda", 0, which=("x", "W"), w_rows=cfg.E + cfg.R * cfg.B)
+    layer = MoEProjection(cfg, "cuda", w_all=d["W"])
+    one = LayerConfig("one_rank", 1, cfg.N, cfg.E, cfg.K, 0, cfg.H, cfg.Hp, cfg.dtype, "infer",
+                      cfg.maxvio)
+    layer1 = MoEProjection(one, "cuda", w_all=d["W"][:cfg.E])
+    out = {}
+    for target in cfg.maxvio:
+        r = make_routing(cfg, target)
+        topk = torch.from_numpy(r.topk_idx).cuda()
+        gates = torch.from_numpy(r.gates).cuda()
+        layer.forward(topk, d["x"], gates)
+        layer1.plan(topk)
+        layer1.dispatch(d["x"])
+        torch.cuda.synchronize()
+        bal = []
+        for q in range(cfg.R):
+            p = balanced_rank(layer, q)
+            bal.append(timed(p.run))
+            del p
+        probs, rows = home_only_ranks(cfg, layer1.xp, layer1.cu_seqlens[0], d["W"])
+        home = [timed(p.run) for p in probs]
+        del probs
+        SK = cfg.S * cfg.K
+        row = {"balanced_rank_us_max": round(max(bal), 1), "balanced_rank_us_mean": round(float(np.mean(bal)), 1),
+               "plain_ep_rank_us_max": round(max(home), 1), "plain_ep_rank_us_mean": round(float(np.mean(home)), 1),
+               "hottest_rank_rows_over_SK": round(max(rows) / SK, 4),
+               "slowdown_plain_over_balanced": round(max(home) / max(bal), 3)}
+        out[f"maxvio={r.maxvio:.3g}"] = row
+        print(f"[home-only] {target}: {row}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 

@@ -248,3 +248,37 @@ def test_whole_layer_graph_capture_replays_match_eager():
         for k, v in want.items():
             assert torch.equal(getattr(layer, k), v), (rep, k)
         assert int(torch.count_nonzero(layer.reduce_buf)) == 0
+
+
+def test_per_rank_subproblems_reproduce_the_full_gemm():
+    """The per-rank views used by the no-redundancy baseline: each balanced rank's
+    one-rank GEMM equals its rows of the full grouped GEMM; each home-only rank's
+    GEMM equals its rows of the one-rank (counting-sort) plan's GEMM; and that plan
+    computes every (token, k) slot to the same bits as the balanced plan."""
+    from redundant_expert_balancing_amd.baseline import balanced_rank, home_only_ranks
+    from redundant_expert_balancing_amd.synth import LayerConfig
+    cfg = CONFIGS["bf16_train_mild"]
+    say("per-rank subproblems", cfg.name)
+    r, layer, d, topk, gates = _setup(cfg, 0.2)
+    layer.forward(topk, d["x"], gates)
+    one = LayerConfig("one_rank", 1, cfg.N, cfg.E, cfg.K, 0, cfg.H, cfg.Hp, cfg.dtype, "infer", (0.2,))
+    layer1 = MoEProjection(one, "cuda", w_all=d["W"][:cfg.E])
+    layer1.forward(topk, d["x"], gates)
+    torch.cuda.synchronize()
+    SK = cfg.S * cfg.K
+    for q in range(cfg.R):
+        p = balanced_rank(layer, q)
+        p.run()
+        torch.cuda.synchronize()
+        assert torch.equal(p.out, layer.out[q * SK:(q + 1) * SK]), q
+    probs, rows = home_only_ranks(cfg, layer1.xp, layer1.cu_seqlens[0], d["W"])
+    assert sum(rows) == cfg.N * cfg.K
+    start = 0
+    for q, p in enumerate(probs):
+        p.run()
+        torch.cuda.synchronize()
+        assert torch.equal(p.out[:rows[q]], layer1.out[start:start + rows[q]]), q
+        start += rows[q]
+    assert torch.equal(layer1.out[layer1.slot_map.long()], layer.out[layer.slot_map.long()])
+    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    assert rows == pl.L
