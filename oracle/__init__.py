@@ -30,4 +30,9 @@ Modules:
             the permute, combine and reduce_grad steps, bfloat16 rounding.
   check  -- an invariant checker that accepts any valid plan without knowing
             the rule.
+  ffn    -- the full expert FFN on the same plan (gate/up projection, SwiGLU,
+            down projection), dense and plan-based, forward and backward, with
+            the layer's rounding points; column-selective helpers for sampled
+            checks at full size. The activation is a reading: the pages name
+            the intermediate size H' but no activation.
 """
