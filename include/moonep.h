@@ -200,6 +200,69 @@ int moonep_reduce_grad(const moonep_shape* shape, const int32_t* replica_expert,
                        float* reduce_buf, float* grad_home, void* stream);
 
 /*
+ * ---- Full expert FFN on the same plan --------------------------------------
+ * The pages give the weight contract per projection, one [E+B, H, H'] tensor
+ * per expert weight, with H' the expert FFN's intermediate size [maestro "The
+ * memory contract"]; they do not name the activation. The FFN built from these
+ * calls is the gated form
+ *     h = x @ W1[e] (gate and up projection),  act = silu(h_gate) * h_up,
+ *     z = act @ W2[e] (down projection),        silu(v) = v / (1 + e^-v),
+ * on two weight views: W1_all [E+R*B, H, 2H'] and W2_all [E+R*B, H', H], both
+ * addressed like W_all and filled by moonep_prefetch_weight with the shapes
+ * below. One plan (cu_seqlens, slot_map, replica_expert) and one workspace
+ * serve every call of the layer:
+ *   up shape    (R,S,E,K,B, H,  2H')  grouped GEMMs of W1, dispatch of x / dy,
+ *                                      combine of dX, reduce_grad of dW1
+ *   down shape  (R,S,E,K,B, H', H )   grouped GEMMs of W2, combine of z,
+ *                                      reduce_grad of dW2
+ *   ffn shape   (R,S,E,K,B, H,  H')   the calls below (Hp = H')
+ * Gate and up columns of W1 (and of h, h_saved and dh) are interleaved in
+ * blocks of MOONEP_SWIGLU_BLOCK: intermediate column p has its gate column at
+ * 2*32*(p / 32) + p % 32 and its up column 32 further. Checkpoints in another
+ * order are permuted once to this layout.
+ */
+enum { MOONEP_SWIGLU_BLOCK = 32 };
+
+/*
+ * SwiGLU of a gate/up projection computed by moonep_grouped_gemm (FWD, up shape).
+ *   h        in   float32 [R*SK, 2*Hp], interleaved gate/up columns
+ *   act      out  dtype [R*SK, Hp]: silu(gate) * up in float32, rounded once to
+ *                 dtype (round to nearest even for bfloat16)
+ *   h_saved  out  NULL, or dtype [R*SK, 2*Hp]: h rounded to dtype, the
+ *                 pre-activation the backward pass reads
+ * Requires Hp a multiple of 32. Rows of unused buffer positions (none in a
+ * valid plan) are processed like any other.
+ */
+int moonep_swiglu(const moonep_shape* shape, const float* h, void* act, void* h_saved,
+                  void* stream);
+
+/*
+ * Gate/up grouped GEMM with the SwiGLU in its epilogue: the same values as
+ * moonep_grouped_gemm(FWD, up shape) followed by moonep_swiglu, bit for bit,
+ * without the float32 h in memory.
+ *   xp       in   dtype [R*SK, H]
+ *   w1_all   in   dtype [E+R*B, H, 2*Hp] (interleaved gate/up columns)
+ *   act      out  dtype [R*SK, Hp];  h_saved  out  NULL or dtype [R*SK, 2*Hp]
+ * Requires H a multiple of 64 and Hp a multiple of 32.
+ */
+int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void* xp, const void* w1_all,
+                               const int32_t* cu_seqlens, void* act, void* h_saved, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * SwiGLU backward: from the saved pre-activation and the gradient of act,
+ *   dh_gate = da * up * silu'(gate),  dh_up = da * silu(gate),
+ *   silu'(v) = s (1 + v (1 - s)),  s = 1 / (1 + e^-v),
+ * in float32, rounded once to dtype.
+ *   h_saved  in   dtype [R*SK, 2*Hp];  da  in  float32 [R*SK, Hp]
+ *   dh       out  dtype [R*SK, 2*Hp] (interleaved), the operand of the
+ *                 backward GEMMs of W1 (DGRAD and WGRAD, up shape)
+ * Requires Hp a multiple of 32. Training layers only.
+ */
+int moonep_swiglu_backward(const moonep_shape* shape, const void* h_saved, const float* da,
+                           void* dh, void* stream);
+
+/*
  * Read (and if `clear`, reset) the sticky device error word of a workspace.
  * Synchronises the device: for tests and debugging, not for the hot path.
  */

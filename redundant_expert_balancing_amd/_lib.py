@@ -24,7 +24,9 @@ EXPORTS = (
     "moonep_version", "moonep_strerror", "moonep_validate_shape", "moonep_workspace_bytes",
     "moonep_workspace_init", "moonep_plan", "moonep_prefetch_weight", "moonep_dispatch",
     "moonep_grouped_gemm", "moonep_combine", "moonep_reduce_grad", "moonep_get_error",
+    "moonep_swiglu", "moonep_grouped_gemm_swiglu", "moonep_swiglu_backward",
 )
+SWIGLU_BLOCK = 32
 
 
 class Shape(ctypes.Structure):
@@ -73,6 +75,10 @@ def lib() -> ctypes.CDLL:
             "moonep_reduce_grad": ([_sp, _vp, _vp, _vp, _vp], ctypes.c_int),
             "moonep_get_error": ([_sp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
                                   ctypes.c_int32], ctypes.c_int),
+            "moonep_swiglu": ([_sp, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "moonep_grouped_gemm_swiglu": ([_sp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                            _vp], ctypes.c_int),
+            "moonep_swiglu_backward": ([_sp, _vp, _vp, _vp, _vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -155,6 +161,22 @@ def moonep_combine(shape, width, src, slot_map, gates, dst, stream=None):
 def moonep_reduce_grad(shape, replica_expert, reduce_buf, grad_home, stream=None):
     _check("moonep_reduce_grad", lib().moonep_reduce_grad(
         ctypes.byref(shape), _p(replica_expert), _p(reduce_buf), _p(grad_home), _s(stream)))
+
+
+def moonep_swiglu(shape, h, act, h_saved=None, stream=None):
+    _check("moonep_swiglu", lib().moonep_swiglu(ctypes.byref(shape), _p(h), _p(act), _p(h_saved),
+                                                _s(stream)))
+
+
+def moonep_grouped_gemm_swiglu(shape, xp, w1_all, cu_seqlens, act, h_saved, ws, stream=None):
+    _check("moonep_grouped_gemm_swiglu", lib().moonep_grouped_gemm_swiglu(
+        ctypes.byref(shape), _p(xp), _p(w1_all), _p(cu_seqlens), _p(act), _p(h_saved), _p(ws),
+        _nbytes(ws), _s(stream)))
+
+
+def moonep_swiglu_backward(shape, h_saved, da, dh, stream=None):
+    _check("moonep_swiglu_backward", lib().moonep_swiglu_backward(
+        ctypes.byref(shape), _p(h_saved), _p(da), _p(dh), _s(stream)))
 
 
 def moonep_get_error(shape, ws, clear: bool = False) -> int:

@@ -53,6 +53,22 @@ inline bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// float32 -> bfloat16 bits, round to nearest, ties to even (finite inputs).
+__device__ inline uint32_t bf16_rne_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// SwiGLU in float32: silu(g) * u with silu(g) = g / (1 + e^-g). Every kernel that
+// produces the activation calls this one function, so all of them agree bit for bit.
+__device__ inline float swiglu_f32(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Gate/up columns of the FFN's first projection are interleaved in blocks of
+// kSwigluBlock: intermediate column p has its gate at 2*kSwigluBlock*(p / kSwigluBlock)
+// + p % kSwigluBlock and its up projection kSwigluBlock further.
+constexpr int kSwigluBlock = MOONEP_SWIGLU_BLOCK;
+
 // Host-side validation shared by all entry points (defined in api.cpp).
 int validate(const moonep_shape* s);
 int elem_bytes(const moonep_shape& s);

@@ -14,6 +14,12 @@
 // contiguous (the weight in FWD, both operands in WGRAD) stay untransposed in
 // LDS and are read with the gfx950 transposing LDS read.
 // fp32 path: a plain FMA kernel per output element (tiny layers only).
+//
+// The gate/up projection of the expert FFN can run with its SwiGLU fused into the
+// epilogue: with gate and up columns interleaved in 32-column blocks, the two
+// 32-column MFMA blocks of one wavefront hold the gate and the up value of the
+// same 32 intermediate columns, so each lane forms silu(gate) * up from its own
+// accumulators and the float32 pre-activation never reaches memory.
 #include <type_traits>
 
 #include "common.h"
@@ -225,14 +231,18 @@ struct GemmArgs {
   const TileEntry* tiles;
   const int32_t* ntiles;
   int H, Hp, E;
+  uint16_t* act;      // SwiGLU epilogue: bf16 [rows, Hp/2]
+  uint16_t* h_saved;  // SwiGLU epilogue: NULL or bf16 [rows, Hp]
 };
 
-template <int OP, int BM, int BN, int WAVES_M, int WAVES_N>
+template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1, "tile shape");
+  static_assert(!SWIGLU || (OP == MOONEP_FWD && WN == 2 * kSwigluBlock && FN == 2),
+                "SwiGLU epilogue: one wavefront holds one gate block and its up block");
   // A stored k-contiguous except in WGRAD; B stored n-contiguous except in DGRAD
   using OA = typename std::conditional<OP == MOONEP_WGRAD, OpMN<BM, NW>, OpK<BM, NW>>::type;
   using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, NW>, OpMN<BN, NW>>::type;
@@ -356,6 +366,46 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 
     // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
     // of each 32 x 32 block; rows past rows_valid fall outside the range.
+    const int r32 = lane & 31;
+    if constexpr (SWIGLU) {
+      // acc[i][0] = gate, acc[i][1] = up of intermediate columns n0/2 + wn*32 + (0..31);
+      // a partial tile ends on a 64-column boundary, so a wavefront is all in or all out
+      const int hact = g.Hp / 2;
+      const int64_t row0 = int64_t(te.rowbase) + m0;
+      const bool live = wn * WN < cols_valid;
+      const __amdgpu_buffer_rsrc_t ars =
+          make_rsrc(g.act + row0 * hact + n0 / 2, clamp_bytes(int64_t(rows_valid) * hact * 2));
+      const uint32_t la = live ? uint32_t(wm * WM + (lane >> 5) * 4) * hact * 2 +
+                                     uint32_t(wn * kSwigluBlock + r32) * 2
+                               : kOffNone;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * hact * 2;
+          const float v = swiglu_f32(acc[i][0][r], acc[i][1][r]);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
+                                                la + rowoff, 0, 0);
+        }
+      if (g.h_saved) {
+        const __amdgpu_buffer_rsrc_t hrs = make_rsrc(
+            g.h_saved + row0 * g.Hp + n0, clamp_bytes(int64_t(rows_valid) * g.Hp * 2));
+        const uint32_t lh = live ? uint32_t(wm * WM + (lane >> 5) * 4) * g.Hp * 2 +
+                                       uint32_t(wn * WN + r32) * 2
+                                 : kOffNone;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * g.Hp * 2;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][r]),
+                                                    hrs, lh + rowoff + j * 64, 0, 0);
+          }
+      }
+      continue;
+    }
     float* cbase;
     uint32_t ldc;
     if (OP == MOONEP_WGRAD) {
@@ -368,7 +418,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       ldc = Ndim;
     }
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
-    const int r32 = lane & 31;
     uint32_t lb[FN];
     const uint32_t lane_row = uint32_t(wm * WM + (lane >> 5) * 4) * ldc * 4;
 #pragma unroll
@@ -433,6 +482,38 @@ __global__ __launch_bounds__(256) void gemm_fp32_kernel(const float* __restrict_
   }
 }
 
+// fp32 gate/up projection with the SwiGLU fused: one thread per (row, intermediate
+// column) forms the gate and the up sums in the same order as gemm_fp32_kernel.
+__global__ __launch_bounds__(256) void gemm_fp32_swiglu_kernel(
+    const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ act,
+    float* __restrict__ h_saved, const TileEntry* __restrict__ tiles,
+    const int32_t* __restrict__ ntiles, int H, int Hact) {
+  const int nt = *ntiles;
+  const int H2 = 2 * Hact;
+  const int64_t wsz = int64_t(H) * H2;
+  for (int t = blockIdx.y; t < nt; t += gridDim.y) {
+    const TileEntry te = tiles[t];
+    const int64_t work = int64_t(te.n) * Hact;
+    for (int64_t idx = blockIdx.x * 256 + threadIdx.x; idx < work; idx += int64_t(gridDim.x) * 256) {
+      const int m = int(idx / Hact), p = int(idx % Hact);
+      const int gc = 2 * kSwigluBlock * (p / kSwigluBlock) + p % kSwigluBlock;
+      const int64_t row = int64_t(te.rowbase) + m;
+      const float* ar = a + row * H;
+      const float* w = b + int64_t(te.wrow) * wsz;
+      float sg = 0.f, su = 0.f;
+      for (int k = 0; k < H; ++k) {
+        sg = fmaf(ar[k], w[int64_t(k) * H2 + gc], sg);
+        su = fmaf(ar[k], w[int64_t(k) * H2 + gc + kSwigluBlock], su);
+      }
+      act[row * Hact + p] = swiglu_f32(sg, su);
+      if (h_saved) {
+        h_saved[row * H2 + gc] = sg;
+        h_saved[row * H2 + gc + kSwigluBlock] = su;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host
 static int device_cus() {
   static int cached_dev = -1, cached = 0;
@@ -455,10 +536,10 @@ struct TileCfg {
   static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, PER_CU = 1;
 };
 
-template <int OP>
+template <int OP, bool SWIGLU = false>
 static void launch_bf16(const GemmArgs& g, int cus, hipStream_t strm) {
   using C = TileCfg<OP>;
-  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N>
+  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU>
       <<<cus * C::PER_CU, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
@@ -499,7 +580,7 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
     const int cus = device_cus();
     if (cus <= 0) return MOONEP_EHIP;
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
-               reduce_buf, tiles, ntiles, s.H, s.Hp, s.E};
+               reduce_buf, tiles, ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
     if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, cus, strm);
     else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, cus, strm);
     else launch_bf16<MOONEP_WGRAD>(g, cus, strm);
@@ -513,6 +594,42 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
       gemm_fp32_kernel<MOONEP_DGRAD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, tiles, ntiles, s.H, s.Hp, s.E);
     else
       gemm_fp32_kernel<MOONEP_WGRAD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, tiles, ntiles, s.H, s.Hp, s.E);
+  }
+  return launch_status();
+}
+
+extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void* xp,
+                                          const void* w1_all, const int32_t* cu_seqlens, void* act,
+                                          void* h_saved, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate(shape);
+  if (st) return st;
+  const moonep_shape& s = *shape;
+  if (s.H % 64 || s.Hp % kSwigluBlock) return MOONEP_EINVAL;
+  if (!aligned16(cu_seqlens) || !aligned16(ws)) return MOONEP_EINVAL;
+  const WsLayout w = ws_layout(s);
+  if (ws_bytes < w.total) return MOONEP_EWORKSPACE;
+  if (s.S == 0) return MOONEP_OK;
+  if (!aligned16(xp) || !aligned16(w1_all) || !aligned16(act)) return MOONEP_EINVAL;
+  if (h_saved && !aligned16(h_saved)) return MOONEP_EINVAL;
+  hipStream_t strm = as_stream(stream);
+  TileEntry* tiles = ws_ptr<TileEntry>(ws, w.tiles);
+  int32_t* ntiles = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount;
+  const bool bf16 = s.dtype == MOONEP_BF16;
+  const int bm = bf16 ? TileCfg<MOONEP_FWD>::BM : 0;
+  gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K, bm, tiles, ntiles,
+                                          int(w.max_tiles));
+  if (launch_status()) return MOONEP_EHIP;
+  if (bf16) {
+    const int cus = device_cus();
+    if (cus <= 0) return MOONEP_EHIP;
+    GemmArgs g{static_cast<const uint16_t*>(xp), static_cast<const uint16_t*>(w1_all), nullptr,
+               nullptr, nullptr, tiles, ntiles, s.H, 2 * s.Hp, s.E,
+               static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved)};
+    launch_bf16<MOONEP_FWD, true>(g, cus, strm);
+  } else {
+    gemm_fp32_swiglu_kernel<<<dim3(64, 256), 256, 0, strm>>>(
+        static_cast<const float*>(xp), static_cast<const float*>(w1_all),
+        static_cast<float*>(act), static_cast<float*>(h_saved), tiles, ntiles, s.H, s.Hp);
   }
   return launch_status();
 }

@@ -17,12 +17,6 @@ namespace moonep {
 constexpr int kMoveThreads = 256;
 constexpr int kMaxK = 32;
 
-__device__ inline uint32_t bf16_rne_bits(float f) {
-  uint32_t b = __float_as_uint(f);
-  b += 0x7FFFu + ((b >> 16) & 1u);  // round to nearest, ties to even
-  return b >> 16;
-}
-
 // Two bf16 values (one 32-bit word) scaled by g in float32, rounded once.
 __device__ inline uint32_t scale_bf16x2(uint32_t w, float g) {
   const float lo = __uint_as_float(w << 16) * g;

@@ -95,8 +95,11 @@ ALPHA = {
 
 
 def stream_seed(seed: int, which: int) -> int:
-    """A 63-bit integer seed for stream ``which`` (0 logits, 1 profile, 2 x, 3 W, 4 dy)."""
-    ss = np.random.SeedSequence(seed).spawn(5)[which]
+    """A 63-bit integer seed for stream ``which`` (0 logits, 1 profile, 2 x, 3 W, 4 dy;
+    for the full expert FFN 5 W1, 6 W2, 7 dy of width H). Child i of a SeedSequence
+    does not depend on how many children are spawned, so streams 0-4 are unchanged
+    by the later ones."""
+    ss = np.random.SeedSequence(seed).spawn(8)[which]
     return int(ss.generate_state(2, dtype=np.uint64)[0] >> np.uint64(1))
 
 
@@ -221,27 +224,35 @@ def calibrate_alpha(cfg: LayerConfig, target: float, seed: int = 0, steps: int =
 
 def make_dense(cfg: LayerConfig, device="cpu", seed: int = 0, which=("x", "W", "dy"),
                w_rows: int | None = None):
-    """x [R*S,H], W [w_rows,H,H'] and dy [R*S,H'] in the layer dtype, drawn on ``device``.
+    """Layer tensors in the layer dtype, drawn on ``device``:
 
-    Only the first E rows of W are drawn (the home experts); ``w_rows`` (default E)
-    may reserve further rows, left uninitialised, for the prefetch slots.
+      x [R*S,H] ~ N(0,1);  W [w_rows,H,H'] ~ N(0,1/H);  dy [R*S,H'] ~ N(0,1)
+      full expert FFN:  W1 [w_rows,H,2H'] ~ N(0,1/H) (gate/up),
+                        W2 [w_rows,H',H] ~ N(0,1/H') (down),  dyH [R*S,H] ~ N(0,1)
+
+    Only the first E rows of a weight are drawn (the home experts); ``w_rows``
+    (default E) may reserve further rows, left uninitialised, for the prefetch slots.
     """
     import torch
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    weights = {"W": (3, cfg.H, cfg.Hp, cfg.H), "W1": (5, cfg.H, 2 * cfg.Hp, cfg.H),
+               "W2": (6, cfg.Hp, cfg.H, cfg.Hp)}
+    rows_of = {"x": (2, cfg.H), "dy": (4, cfg.Hp), "dyH": (7, cfg.H)}
     out = {}
     for name in which:
         g = torch.Generator(device=device)
-        if name == "W":
-            g.manual_seed(stream_seed(seed, 3))
+        if name in weights:
+            stream, d0, d1, fan_in = weights[name]
+            g.manual_seed(stream_seed(seed, stream))
             rows = cfg.E if w_rows is None else w_rows
-            t = torch.empty((rows, cfg.H, cfg.Hp), dtype=dt, device=device)
-            buf = torch.empty((cfg.H, cfg.Hp), dtype=torch.float32, device=device)
+            t = torch.empty((rows, d0, d1), dtype=dt, device=device)
+            buf = torch.empty((d0, d1), dtype=torch.float32, device=device)
             for e in range(cfg.E):      # expert by expert: fp32 staging stays small
-                buf.normal_(0.0, cfg.H ** -0.5, generator=g)
+                buf.normal_(0.0, fan_in ** -0.5, generator=g)
                 t[e].copy_(buf)
-        elif name in ("x", "dy"):
-            g.manual_seed(stream_seed(seed, 2 if name == "x" else 4))
-            width = cfg.H if name == "x" else cfg.Hp
+        elif name in rows_of:
+            stream, width = rows_of[name]
+            g.manual_seed(stream_seed(seed, stream))
             buf = torch.empty((cfg.N, width), dtype=torch.float32, device=device)
             buf.normal_(0.0, 1.0, generator=g)
             t = buf.to(dt)

@@ -80,3 +80,25 @@ def rel_err(got, ref):
 def tolerance(cfg) -> float:
     # max abs error <= 1e-2 * RMS(reference) for bf16 layers, 1e-5 * RMS for fp32
     return 1e-2 if cfg.dtype == "bf16" else 1e-5
+
+
+def assert_stored_close(got, ref, dtype, what=""):
+    """An intermediate the layer stores in its dtype (the SwiGLU output, the saved
+    pre-activation), element by element: within one rounding step of the stored
+    type of the oracle's value (2^-7 relative for bfloat16, 2^-22 for float32) plus
+    the float32 accumulation-order error upstream of the rounding, which shows where
+    the value is near zero (1e-4 * RMS(ref) for bfloat16 layers, whose bar is
+    1e-2 * RMS; 1e-5 * RMS for float32 layers).
+    (A max-abs / RMS bound does not fit such tensors: where the float32 and the
+    float64 sums straddle a rounding boundary the stored value moves by a whole
+    step of that element, and the largest elements are many RMS.)"""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    step = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -22
+    rms = np.sqrt(np.mean(ref * ref))
+    floor = 1e-4 if dtype == "bf16" else 1e-5
+    bad = np.abs(got - ref) > step * np.abs(ref) + floor * rms
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements off, first at {i}: "
+                             f"got {got[i]!r} want {ref[i]!r} (RMS {rms:.4g})")

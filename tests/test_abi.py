@@ -88,3 +88,24 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert lib.moonep_reduce_grad(ctypes.byref(inf), p, p, p, None) == L.EMODE
     odd = S(H=96, Hp=64)              # bf16 GEMM needs multiples of 64
     assert lib.moonep_grouped_gemm(ctypes.byref(odd), L.FWD, p, p, p, p, None, None, p, 1 << 30, None) == L.EINVAL
+
+
+def test_ffn_entry_points_validate_before_launch():
+    lib = L.lib()
+    p = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1008)
+    sh = S(H=128, Hp=64)
+    assert lib.moonep_swiglu(ctypes.byref(S(Hp=48)), p, p, None, None) == L.EINVAL  # Hp % 32
+    assert lib.moonep_swiglu(ctypes.byref(sh), bad, p, None, None) == L.EINVAL
+    assert lib.moonep_swiglu(ctypes.byref(sh), p, p, bad, None) == L.EINVAL
+    assert lib.moonep_swiglu(ctypes.byref(S(S=0)), None, None, None, None) == L.OK
+    inf = S(mode=L.INFER, B=2)
+    assert lib.moonep_swiglu_backward(ctypes.byref(inf), p, p, p, None) == L.EMODE
+    assert lib.moonep_swiglu_backward(ctypes.byref(sh), p, None, p, None) == L.EINVAL
+    assert lib.moonep_grouped_gemm_swiglu(ctypes.byref(S(H=96)), p, p, p, p, None, p, 1 << 30,
+                                          None) == L.EINVAL
+    assert lib.moonep_grouped_gemm_swiglu(ctypes.byref(sh), p, p, p, p, None, p, 16,
+                                          None) == L.EWORKSPACE
+    assert lib.moonep_grouped_gemm_swiglu(ctypes.byref(sh), p, p, p, bad, None, p, 1 << 30,
+                                          None) == L.EINVAL
+    assert L.SWIGLU_BLOCK == 32
