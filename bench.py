@@ -50,6 +50,10 @@ def parse():
                     help="only print per-stage microseconds for every layer configuration")
     ap.add_argument("--home-only-baseline", action="store_true",
                     help="only print per-rank grouped-GEMM time, balanced vs plain EP")
+    ap.add_argument("--ffn", action="store_true",
+                    help="only print per-stage microseconds of the full expert FFN (gate/up "
+                         "with SwiGLU, down) forward at the bench shape and backward at the "
+                         "training-backward shape")
     return ap.parse_args()
 
 
@@ -145,6 +149,9 @@ def main():
         return
     if args.home_only_baseline:
         home_only_baseline(args.stage_reps)
+        return
+    if args.ffn:
+        ffn_table(args.stage_reps)
         return
     L.lib()   # fail loudly if the HIP library is missing
 
@@ -395,6 +402,115 @@ def home_only_baseline(reps):
         out[f"maxvio={r.maxvio:.3g}"] = row
         print(f"[home-only] {target}: {row}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
+def _timer(reps):
+    """Median microseconds of fn over reps runs, each after a 1 GiB write that
+    evicts the caches, timed with HIP events on the current stream."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return round(float(np.median(ts)), 1)
+    return timed
+
+
+def ffn_table(reps):
+    """The full expert FFN on the balanced plan: forward stages at the bench shape
+    for every imbalance point (plus the unfused gate/up GEMM + SwiGLU pass once),
+    backward stages at the training-backward shape; TFLOP/s of every GEMM and
+    GB/s of the SwiGLU passes."""
+    import torch
+
+    from redundant_expert_balancing_amd import _lib as L
+    from redundant_expert_balancing_amd.ffn import MoEFFN
+    from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
+
+    timed = _timer(reps)
+    out = {}
+
+    def tf(flop, us):
+        return round(flop / (us * 1e-6) / 1e12, 1)
+
+    cfg = CONFIGS["bench_shape"]
+    d = make_dense(cfg, "cuda", 0, which=("x", "W1", "W2"), w_rows=cfg.E + cfg.R * cfg.B)
+    layer = MoEFFN(cfg, "cuda", w1_all=d["W1"], w2_all=d["W2"])
+    slots = cfg.N * cfg.K
+    f_up, f_down = 2.0 * slots * cfg.H * 2 * cfg.Hp, 2.0 * slots * cfg.Hp * cfg.H
+    for i, target in enumerate(cfg.maxvio):
+        r = make_routing(cfg, target)
+        topk = torch.from_numpy(r.topk_idx).cuda()
+        gates = torch.from_numpy(r.gates).cuda()
+        layer.forward(topk, d["x"], gates)
+        row = {"plan": timed(lambda: layer.plan(topk)),
+               "prefetch_w1_w2": timed(layer.prefetch),
+               "dispatch": timed(lambda: layer.dispatch(d["x"])),
+               "gate_up_swiglu": timed(layer.gate_up),
+               "down": timed(layer.down_proj),
+               "combine": timed(lambda: layer.combine(gates))}
+        row["gate_up_tflops"] = tf(f_up, row["gate_up_swiglu"])
+        row["down_tflops"] = tf(f_down, row["down"])
+        t = row["plan"] + row["dispatch"] + row["gate_up_swiglu"] + row["down"] + row["combine"]
+        row["ffn_tokens_per_s"] = round(cfg.N / (t * 1e-6), 1)
+        row["replicas"] = int((layer.replica_expert[:, :cfg.B] >= 0).sum())
+        if i == 0:
+            # the same projection unfused: GEMM to float32 h, then the SwiGLU pass
+            h = torch.empty((slots, 2 * cfg.Hp), dtype=torch.float32, device="cuda")
+            row["unfused_gemm"] = timed(lambda: L.moonep_grouped_gemm(
+                layer.up, L.FWD, layer.xp, layer.w1_all, layer.cu_seqlens, h, None, None, layer.ws))
+            row["unfused_swiglu"] = timed(lambda: L.moonep_swiglu(layer.shape, h, layer.act, None))
+            sw_bytes = slots * (2 * cfg.Hp * 4 + cfg.Hp * 2)
+            row["swiglu_gbs"] = round(sw_bytes / (row["unfused_swiglu"] * 1e-6) / 1e9, 1)
+            del h
+        out[f"fwd {cfg.name} maxvio={r.maxvio:.3g}"] = row
+        print(f"[ffn] fwd {target}: {row}", file=sys.stderr, flush=True)
+    del layer, d
+    torch.cuda.empty_cache()
+
+    cfg = CONFIGS["train_backward"]
+    d = make_dense(cfg, "cuda", 0, which=("x", "W1", "W2", "dyH"), w_rows=cfg.E + cfg.R * cfg.B)
+    layer = MoEFFN(cfg, "cuda", backward=True, w1_all=d["W1"], w2_all=d["W2"])
+    slots = cfg.N * cfg.K
+    f_up, f_down = 2.0 * slots * cfg.H * 2 * cfg.Hp, 2.0 * slots * cfg.Hp * cfg.H
+    for target in cfg.maxvio:
+        r = make_routing(cfg, target)
+        topk = torch.from_numpy(r.topk_idx).cuda()
+        gates = torch.from_numpy(r.gates).cuda()
+        layer.forward(topk, d["x"], gates)
+        layer.backward(d["dyH"], gates)
+        up, dn, sh = layer.up, layer.down, layer.shape
+        row = {"gate_up_swiglu": timed(layer.gate_up), "down": timed(layer.down_proj),
+               "dispatch_dy": timed(lambda: L.moonep_dispatch(up, cfg.H, d["dyH"], layer.slot_map, gates, layer.dyp)),
+               "dgrad_down": timed(lambda: L.moonep_grouped_gemm(dn, L.DGRAD, layer.dyp, layer.w2_all, layer.cu_seqlens, layer.da, None, None, layer.ws)),
+               "wgrad_down": timed(lambda: L.moonep_grouped_gemm(dn, L.WGRAD, layer.act, layer.dyp, layer.cu_seqlens, None, layer.grad2, layer.red2, layer.ws)),
+               "swiglu_backward": timed(lambda: L.moonep_swiglu_backward(sh, layer.hs, layer.da, layer.dh)),
+               "dgrad_up": timed(lambda: L.moonep_grouped_gemm(up, L.DGRAD, layer.dh, layer.w1_all, layer.cu_seqlens, layer.dxp, None, None, layer.ws)),
+               "wgrad_up": timed(lambda: L.moonep_grouped_gemm(up, L.WGRAD, layer.xp, layer.dh, layer.cu_seqlens, None, layer.grad1, layer.red1, layer.ws)),
+               "unpermute": timed(lambda: L.moonep_combine(up, cfg.H, layer.dxp, layer.slot_map, None, layer.dx)),
+               "reduce_grad_w1_w2": timed(lambda: (L.moonep_reduce_grad(up, layer.replica_expert, layer.red1, layer.grad1),
+                                                    L.moonep_reduce_grad(dn, layer.replica_expert, layer.red2, layer.grad2)))}
+        for k, f in (("gate_up_swiglu", f_up), ("down", f_down), ("dgrad_down", f_down),
+                     ("wgrad_down", f_down), ("dgrad_up", f_up), ("wgrad_up", f_up)):
+            row[k + "_tflops"] = tf(f, row[k])
+        sb = slots * (2 * cfg.Hp * 2 + cfg.Hp * 4 + 2 * cfg.Hp * 2)
+        row["swiglu_backward_gbs"] = round(sb / (row["swiglu_backward"] * 1e-6) / 1e9, 1)
+        row["replicas"] = int((layer.replica_expert[:, :cfg.B] >= 0).sum())
+        out[f"bwd {cfg.name} maxvio={r.maxvio:.3g}"] = row
+        print(f"[ffn] bwd {target}: {row}", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
