@@ -50,6 +50,9 @@ def parse():
                     help="only print per-stage microseconds for every layer configuration")
     ap.add_argument("--home-only-baseline", action="store_true",
                     help="only print per-rank grouped-GEMM time, balanced vs plain EP")
+    ap.add_argument("--stack", type=int, default=0,
+                    help="only time N layers at the bench shape whose prefetch slots share one "
+                         "pool, prefetch serial vs on a side stream overlapped with dispatch")
     ap.add_argument("--ffn", action="store_true",
                     help="only print per-stage microseconds of the full expert FFN (gate/up "
                          "with SwiGLU, down) forward at the bench shape and backward at the "
@@ -152,6 +155,9 @@ def main():
         return
     if args.ffn:
         ffn_table(args.stage_reps)
+        return
+    if args.stack:
+        stack_bench(args.stack, args.steps, args.warmup)
         return
     L.lib()   # fail loudly if the HIP library is missing
 
@@ -427,6 +433,103 @@ def _timer(reps):
             ts.append(a.elapsed_time(b) * 1e3)
         return round(float(np.median(ts)), 1)
     return timed
+
+
+def stack_bench(n_layers, steps, warmup):
+    """Layers whose slots come from one process-global pool.
+
+    Forward, bench shape: n_layers layers (own weights and router output, the
+    imbalance points in turn), one slot set, the prefetch on the main stream or
+    on a side stream overlapped with dispatch.
+    Backward, training-backward shape: the stack's backward with one set and the
+    prefetches serial, against two sets with the next layer's prefetch on the side
+    stream under the current layer's GEMMs.
+    Milliseconds per layer (median of ``steps`` passes) and slot memory against
+    private per-layer slots."""
+    import numpy as np
+    import torch
+
+    from redundant_expert_balancing_amd.pool import MoEStack
+    from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
+
+    main = torch.cuda.current_stream()
+
+    def time_passes(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            fn()
+            b.record(main)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / n_layers)
+        return round(float(np.median(ts)), 4)
+
+    def build(cfg, nsets, backward):
+        stack = MoEStack(cfg, n_layers, backward=backward, nsets=nsets)
+        d = make_dense(cfg, "cuda", 0, which=("x", "W", "dy") if backward else ("x", "W"))
+        ins = []
+        for l in range(n_layers):
+            r = make_routing(cfg, cfg.maxvio[l % len(cfg.maxvio)])
+            stack.layers[l].w_all[:cfg.E].copy_(d["W"])
+            ins.append((torch.from_numpy(r.topk_idx).cuda(), torch.from_numpy(r.gates).cuda()))
+        del d["W"]
+        return stack, d, ins
+
+    out = {"layers": n_layers}
+    cfg = CONFIGS["bench_shape"]
+    stack, d, ins = build(cfg, 1, False)
+    out["fwd_pool_bytes"] = stack.pool.nbytes
+    out["fwd_private_slot_bytes"] = n_layers * cfg.R * cfg.B * cfg.H * cfg.Hp * 2
+
+    def fwd():
+        for l in range(n_layers):
+            stack.forward_layer(l, ins[l][0], d["x"], ins[l][1])
+    for mode in ("serial", "side_stream"):
+        stack.overlap_forward = mode == "side_stream"
+        out[f"fwd_{cfg.name}_{mode}_ms_per_layer"] = time_passes(fwd)
+        print(f"[stack] {out}", file=sys.stderr, flush=True)
+    assert all(layer.error_flags() == 0 for layer in stack.layers)
+    stack.close()
+    del stack, d, ins
+    torch.cuda.empty_cache()
+
+    cfg = CONFIGS["train_backward"]
+    for nsets, overlap in ((1, False), (2, True)):
+        stack, d, ins = build(cfg, nsets, True)
+        stack.overlap_forward, stack.overlap_backward = False, overlap
+
+        def bwd():
+            for l in range(n_layers):
+                stack.forward_layer(l, ins[l][0], d["x"], ins[l][1])
+            torch.cuda.synchronize()
+            return None
+
+        # the backward alone is timed; each pass re-runs the forward untimed first
+        ts = []
+        for it in range(warmup + steps):
+            bwd()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            for l in reversed(range(n_layers)):
+                stack.backward_layer(l, d["dy"], ins[l][1])
+            b.record(main)
+            torch.cuda.synchronize()
+            if it >= warmup:
+                ts.append(a.elapsed_time(b) / n_layers)
+        key = f"bwd_{cfg.name}_{nsets}set_{'side_stream' if overlap else 'serial'}"
+        out[key + "_ms_per_layer"] = round(float(np.median(ts)), 4)
+        out[key + "_pool_bytes"] = stack.pool.nbytes
+        print(f"[stack] {out}", file=sys.stderr, flush=True)
+        stack.close()
+        del stack, d, ins
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 def ffn_table(reps):

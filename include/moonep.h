@@ -263,6 +263,51 @@ int moonep_swiglu_backward(const moonep_shape* shape, const void* h_saved, const
                            void* dh, void* stream);
 
 /*
+ * ---- Process-global prefetch-slot pool ----------------------------------------
+ * The prefetch slots of every layer come from one process-global pool, so the
+ * extra memory is R*B expert weights per projection in total, not per layer,
+ * while each layer still hands the grouped GEMM one contiguous [E+R*B, H, Hp]
+ * tensor [maestro "The memory contract": prefetch slots drawn from a
+ * process-global pool shared by all layers; noticiai "O contrato de memória"].
+ * A view is one reserved virtual address range: rows [0,E) map the layer's own
+ * home-weight allocation (owned by the view), rows [E, E+R*B) map one physical
+ * set of the pool. The view's base address is the w_all every other call takes.
+ * Views of the same pool set alias the same slot memory: a layer's slots hold
+ * its replicas only from its moonep_prefetch_weight until another layer's
+ * prefetch on that set; a backward pass prefetches its layer's replicas again.
+ *
+ * These calls ALLOCATE (device virtual memory) and synchronise where stated;
+ * they are set-up calls, not hot-path calls. Home rows start uninitialised.
+ * Requires HIP virtual memory support; E*H*Hp*element_size must be a multiple
+ * of moonep_vm_granularity() (MOONEP_EINVAL otherwise).
+ */
+typedef struct moonep_pool moonep_pool;
+typedef struct moonep_view moonep_view;
+
+/* Virtual-memory mapping granularity of the current device in bytes, 0 if the
+ * device has no virtual memory support. */
+size_t moonep_vm_granularity(void);
+
+/* A pool of `nsets` physical slot sets (1..64), each R*B rows of H*Hp elements of
+ * shape->dtype, on the current device. B >= 1. */
+int moonep_pool_create(const moonep_shape* shape, int32_t nsets, moonep_pool** pool);
+
+/* Physical bytes the pool holds (all sets). */
+size_t moonep_pool_bytes(const moonep_pool* pool);
+
+/* Release the pool. Every view on it must be destroyed first. */
+int moonep_pool_destroy(moonep_pool* pool);
+
+/* A layer's [E+R*B, H, Hp] view: fresh home rows plus slot set `set` of `pool`.
+ * shape must match the pool's R, B, H, Hp and dtype (E may differ). *w_all
+ * receives the view's device address. */
+int moonep_view_create(const moonep_shape* shape, moonep_pool* pool, int32_t set,
+                       moonep_view** view, void** w_all);
+
+/* Synchronise the device, unmap the view and free its home rows. */
+int moonep_view_destroy(moonep_view* view);
+
+/*
  * Read (and if `clear`, reset) the sticky device error word of a workspace.
  * Synchronises the device: for tests and debugging, not for the hot path.
  */

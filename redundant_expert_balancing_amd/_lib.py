@@ -25,6 +25,8 @@ EXPORTS = (
     "moonep_workspace_init", "moonep_plan", "moonep_prefetch_weight", "moonep_dispatch",
     "moonep_grouped_gemm", "moonep_combine", "moonep_reduce_grad", "moonep_get_error",
     "moonep_swiglu", "moonep_grouped_gemm_swiglu", "moonep_swiglu_backward",
+    "moonep_vm_granularity", "moonep_pool_create", "moonep_pool_bytes", "moonep_pool_destroy",
+    "moonep_view_create", "moonep_view_destroy",
 )
 SWIGLU_BLOCK = 32
 
@@ -79,6 +81,13 @@ def lib() -> ctypes.CDLL:
             "moonep_grouped_gemm_swiglu": ([_sp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                             _vp], ctypes.c_int),
             "moonep_swiglu_backward": ([_sp, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "moonep_vm_granularity": ([], ctypes.c_size_t),
+            "moonep_pool_create": ([_sp, ctypes.c_int32, ctypes.POINTER(_vp)], ctypes.c_int),
+            "moonep_pool_bytes": ([_vp], ctypes.c_size_t),
+            "moonep_pool_destroy": ([_vp], ctypes.c_int),
+            "moonep_view_create": ([_sp, _vp, ctypes.c_int32, ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_vp)], ctypes.c_int),
+            "moonep_view_destroy": ([_vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -177,6 +186,38 @@ def moonep_grouped_gemm_swiglu(shape, xp, w1_all, cu_seqlens, act, h_saved, ws, 
 def moonep_swiglu_backward(shape, h_saved, da, dh, stream=None):
     _check("moonep_swiglu_backward", lib().moonep_swiglu_backward(
         ctypes.byref(shape), _p(h_saved), _p(da), _p(dh), _s(stream)))
+
+
+def moonep_vm_granularity() -> int:
+    return lib().moonep_vm_granularity()
+
+
+def moonep_pool_create(shape, nsets: int) -> int:
+    """Opaque pool handle (an int address)."""
+    h = _vp()
+    _check("moonep_pool_create", lib().moonep_pool_create(ctypes.byref(shape), int(nsets),
+                                                          ctypes.byref(h)))
+    return h.value
+
+
+def moonep_pool_bytes(pool) -> int:
+    return lib().moonep_pool_bytes(_vp(pool))
+
+
+def moonep_pool_destroy(pool):
+    _check("moonep_pool_destroy", lib().moonep_pool_destroy(_vp(pool)))
+
+
+def moonep_view_create(shape, pool, set_index: int):
+    """(view handle, device address of the [E+R*B, H, Hp] view)."""
+    v, w = _vp(), _vp()
+    _check("moonep_view_create", lib().moonep_view_create(
+        ctypes.byref(shape), _vp(pool), int(set_index), ctypes.byref(v), ctypes.byref(w)))
+    return v.value, w.value
+
+
+def moonep_view_destroy(view):
+    _check("moonep_view_destroy", lib().moonep_view_destroy(_vp(view)))
 
 
 def moonep_get_error(shape, ws, clear: bool = False) -> int:

@@ -109,3 +109,18 @@ def test_ffn_entry_points_validate_before_launch():
     assert lib.moonep_grouped_gemm_swiglu(ctypes.byref(sh), p, p, p, bad, None, p, 1 << 30,
                                           None) == L.EINVAL
     assert L.SWIGLU_BLOCK == 32
+
+
+def test_pool_calls_validate_before_any_hip_call():
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    assert lib.moonep_pool_create(ctypes.byref(S(mode=L.INFER, B=0)), 1, ctypes.byref(h)) == L.EINVAL
+    assert lib.moonep_pool_create(ctypes.byref(S()), 0, ctypes.byref(h)) == L.EINVAL
+    assert lib.moonep_pool_create(ctypes.byref(S()), 65, ctypes.byref(h)) == L.EINVAL
+    assert lib.moonep_pool_create(ctypes.byref(S(E=18)), 1, ctypes.byref(h)) == L.EINVAL
+    assert lib.moonep_pool_create(ctypes.byref(S()), 1, None) == L.EINVAL
+    v, w = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.moonep_view_create(ctypes.byref(S()), None, 0, ctypes.byref(v), ctypes.byref(w)) == L.EINVAL
+    assert lib.moonep_pool_destroy(None) == L.EINVAL
+    assert lib.moonep_view_destroy(None) == L.EINVAL
+    assert lib.moonep_pool_bytes(None) == 0
