@@ -12,7 +12,11 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation; operands go
 // global -> LDS by DMA into a ring of k-steps; operands stored with M or N
 // contiguous (the weight in FWD, both operands in WGRAD) stay untransposed in
-// LDS and are read with the gfx950 transposing LDS read.
+// LDS and are read with the gfx950 transposing LDS read. Each wavefront holds the
+// fragments of the step it multiplies in registers and refills them from the
+// next step right behind its MFMAs (one LDS read between consecutive MFMAs), so
+// the per-step barrier does not drain the MFMA pipe and a ring stage is free one
+// step earlier: the DMAs run three steps ahead in a four-stage ring.
 // fp32 path: a plain FMA kernel per output element (tiny layers only).
 //
 // The gate/up projection of the expert FFN can run with its SwiGLU fused into the
@@ -241,8 +245,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1, "tile shape");
-  static_assert(!SWIGLU || (OP == MOONEP_FWD && WN == 2 * kSwigluBlock && FN == 2),
-                "SwiGLU epilogue: one wavefront holds one gate block and its up block");
+  static_assert(!SWIGLU || (OP == MOONEP_FWD && FN % 2 == 0 && kSwigluBlock == 32),
+                "SwiGLU epilogue: a wavefront holds whole (gate, up) block pairs");
   // A stored k-contiguous except in WGRAD; B stored n-contiguous except in DGRAD
   using OA = typename std::conditional<OP == MOONEP_WGRAD, OpMN<BM, NW>, OpK<BM, NW>>::type;
   using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, NW>, OpMN<BN, NW>>::type;
@@ -326,73 +330,99 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     // every wavefront has finished reading the ring (previous tile) before refilling it
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
+    for (int p = 0; p < kStages; ++p)
       if (p < kiters) issue(p);
 
-    auto compute = [&](int kt) {
+    constexpr int KS = kBK / 16;
+    bf16x8_t fa[KS][FM], fb[KS][FN];
+    // fragments of 16-deep substep ks of step kt
+    auto load = [&](int kt, int ks) {
       const char* st = smem + (kt % kStages) * STAGE;
 #pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        bf16x8_t af[FM], bfr[FN];
+      for (int i = 0; i < FM; ++i) fa[ks][i] = OA::frag(st, wm * WM + i * 32, ks, lane);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = OA::frag(st, wm * WM + i * 32, ks, lane);
+      for (int j = 0; j < FN; ++j) fb[ks][j] = OB::frag(st + OA::BYTES, wn * WN + j * 32, ks, lane);
+    };
+    // wait until at most `later` newer steps' DMAs of this wavefront are in flight
+    auto wait_dma = [&](int later) {
+      if (later >= 3) wait_vm<3 * DMA_PER_STEP>();
+      else if (later == 2) wait_vm<2 * DMA_PER_STEP>();
+      else if (later == 1) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
+    };
+    // before the first barrier, steps 0 .. min(kiters, kStages) - 1 are issued
+    wait_dma(min(kiters - 1, kStages - 1));
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[j] = OB::frag(st + OA::BYTES, wn * WN + j * 32, ks, lane);
+    for (int ks = 0; ks < KS; ++ks) load(0, ks);
+    // step kt: the fragments of step kt are in registers; before its barrier, steps
+    // up to min(kiters - 1, kt + kStages - 1) are issued. The MFMAs of substep ks
+    // are issued, then its registers are refilled from step kt+1, so LDS reads run
+    // under the MFMAs and the MFMA pipe is not drained at the barrier.
+    for (int kt = 0; kt < kiters; ++kt) {
+      const bool more = kt + 1 < kiters;
+      if (more) wait_dma(min(kiters - kt - 2, kStages - 2));
+      // step kt+1 is visible to every wavefront; every wavefront's reads of step kt
+      // have completed, so stage kt % kStages can be refilled
+      __syncthreads();
+      if (kt + kStages < kiters) issue(kt + kStages);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+        // refill (after the last step: re-read this step, in bounds and unused), one
+        // LDS read between consecutive MFMAs
+        load(more ? kt + 1 : kt, ks);
+#pragma unroll
+        for (int q = 0; q < FM * FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
       }
-    };
-    // steady state: kStages-2 later steps stay in flight while step kt is consumed
-    int kt = 0;
-    for (; kt + kStages - 2 < kiters; ++kt) {
-      wait_vm<(kStages - 2) * DMA_PER_STEP>();
-      __syncthreads();
-      // the stage refilled here was last read in step kt-1, finished by everyone
-      if (kt + kStages - 1 < kiters) issue(kt + kStages - 1);
-      compute(kt);
-    }
-    // tail: fewer steps in flight
-    for (; kt < kiters; ++kt) {
-      const int ahead = kiters - 1 - kt;   // < kStages - 2
-      if (ahead >= 2) wait_vm<2 * DMA_PER_STEP>();
-      else if (ahead == 1) wait_vm<DMA_PER_STEP>();
-      else wait_vm<0>();
-      __syncthreads();
-      compute(kt);
     }
 
     // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
     // of each 32 x 32 block; rows past rows_valid fall outside the range.
     const int r32 = lane & 31;
     if constexpr (SWIGLU) {
-      // acc[i][0] = gate, acc[i][1] = up of intermediate columns n0/2 + wn*32 + (0..31);
-      // a partial tile ends on a 64-column boundary, so a wavefront is all in or all out
+      // block pair (2jp, 2jp+1) of the wavefront = (gate, up) of intermediate columns
+      // n0/2 + wn*WN/2 + jp*32 + (0..31); a partial tile ends on a 64-column boundary,
+      // so each pair is all in or all out
       const int hact = g.Hp / 2;
       const int64_t row0 = int64_t(te.rowbase) + m0;
-      const bool live = wn * WN < cols_valid;
       const __amdgpu_buffer_rsrc_t ars =
           make_rsrc(g.act + row0 * hact + n0 / 2, clamp_bytes(int64_t(rows_valid) * hact * 2));
-      const uint32_t la = live ? uint32_t(wm * WM + (lane >> 5) * 4) * hact * 2 +
-                                     uint32_t(wn * kSwigluBlock + r32) * 2
-                               : kOffNone;
+      const uint32_t arow = uint32_t(wm * WM + (lane >> 5) * 4) * hact * 2;
+      uint32_t la[FN / 2];
+#pragma unroll
+      for (int jp = 0; jp < FN / 2; ++jp)
+        la[jp] = wn * WN + jp * 64 < cols_valid
+                     ? arow + uint32_t(wn * (WN / 2) + jp * kSwigluBlock + r32) * 2
+                     : kOffNone;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * hact * 2;
-          const float v = swiglu_f32(acc[i][0][r], acc[i][1][r]);
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
-                                                la + rowoff, 0, 0);
+#pragma unroll
+          for (int jp = 0; jp < FN / 2; ++jp) {
+            const float v = swiglu_f32(acc[i][2 * jp][r], acc[i][2 * jp + 1][r]);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
+                                                  la[jp] + rowoff, 0, 0);
+          }
         }
       if (g.h_saved) {
         const __amdgpu_buffer_rsrc_t hrs = make_rsrc(
             g.h_saved + row0 * g.Hp + n0, clamp_bytes(int64_t(rows_valid) * g.Hp * 2));
-        const uint32_t lh = live ? uint32_t(wm * WM + (lane >> 5) * 4) * g.Hp * 2 +
-                                       uint32_t(wn * WN + r32) * 2
-                                 : kOffNone;
+        const uint32_t hrow = uint32_t(wm * WM + (lane >> 5) * 4) * g.Hp * 2;
+        uint32_t lh[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          lh[j] = wn * WN + (j / 2) * 64 < cols_valid ? hrow + uint32_t(wn * WN + j * 32 + r32) * 2
+                                                      : kOffNone;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -401,7 +431,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 #pragma unroll
             for (int j = 0; j < FN; ++j)
               __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][r]),
-                                                    hrs, lh + rowoff + j * 64, 0, 0);
+                                                    hrs, lh[j] + rowoff, 0, 0);
           }
       }
       continue;
@@ -529,8 +559,10 @@ static int device_cus() {
 }
 
 // bf16 tile configuration: 256 x 256 output tiles, 8 wavefronts (two per SIMD, so
-// one wavefront's LDS reads and waits overlap the other's MFMAs) of 128 x 64,
-// 32-deep k-steps in a 4-stage LDS ring (128 KiB), one workgroup per CU.
+// one wavefront's waits overlap the other's MFMAs) of 128 x 64, 32-deep k-steps in
+// a 4-stage LDS ring (128 KiB), one workgroup per CU. Four wavefronts of 128 x 128
+// (a third fewer LDS bytes per flop) measured 5% slower: one wavefront per SIMD
+// leaves every barrier exposed.
 template <int OP>
 struct TileCfg {
   static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, PER_CU = 1;
