@@ -12,6 +12,8 @@ namespace moonep {
 // Router tokens per planning chunk: one 64-wide wavefront owns a chunk, one lane
 // per token while counting, 64 consecutive slots per step while assigning.
 constexpr int kChunkTokens = 64;
+// Chunks per partition of the planner's column scan (16 wavefronts x 4 chunks).
+constexpr int kScanPart = 64;
 // Smallest GEMM M tile; sizes the tile list in the workspace.
 constexpr int kMinTileM = 64;
 
@@ -19,8 +21,8 @@ constexpr int kMinTileM = 64;
 enum FlagWord { kFlagError = 0, kFlagPlanValid = 1, kFlagTileCount = 2, kFlagWords = 64 };
 
 struct WsLayout {
-  size_t flags, T, counts, piece_ptr, piece_tlo, piece_base, tiles, total;
-  int64_t nchunk, max_pieces, max_tiles;
+  size_t flags, part, counts, piece_ptr, piece_tlo, piece_base, tiles, total;
+  int64_t nchunk, npart, max_pieces, max_tiles;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -30,11 +32,12 @@ inline WsLayout ws_layout(const moonep_shape& s) {
   const int64_t N = int64_t(s.R) * s.S;
   const int64_t SK = int64_t(s.S) * s.K;
   w.nchunk = (N + kChunkTokens - 1) / kChunkTokens;
+  w.npart = (w.nchunk + kScanPart - 1) / kScanPart;
   w.max_pieces = int64_t(s.E) + 2 * int64_t(s.R) + 8;
   w.max_tiles = int64_t(s.R) * ((SK + kMinTileM - 1) / kMinTileM + s.E + s.B) + 1;
   size_t o = 0;
   w.flags = o;      o = align256(o + kFlagWords * 4);
-  w.T = o;          o = align256(o + size_t(s.E) * 4);
+  w.part = o;       o = align256(o + size_t(w.npart) * s.E * 4);
   w.counts = o;     o = align256(o + size_t(w.nchunk) * s.E * 4);
   w.piece_ptr = o;  o = align256(o + size_t(s.E + 1) * 4);
   w.piece_tlo = o;  o = align256(o + size_t(w.max_pieces) * 4);

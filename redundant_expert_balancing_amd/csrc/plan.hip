@@ -9,8 +9,11 @@
 //
 //   count   one wavefront per chunk of 64 tokens: per-chunk expert histogram
 //           (LDS atomics) into counts[chunk][E]; flags bad or repeated ids.
-//   scan    column-wise exclusive prefix of counts over chunks (the base rank
-//           of each chunk's first slot of every expert), T[e] = column total.
+//   scan    column-wise exclusive prefix of counts over the chunks of each
+//           partition of kScanPart chunks, and the partition totals.
+//           (The solve kernel folds the partition totals into T[e] and a
+//           prefix over partitions; assign adds that prefix: together the base
+//           rank of each chunk's first slot of every expert.)
 //   solve   one workgroup: rank loads, donor tree, per-donor expert layout,
 //           pieces, prefetch slots, cu_seqlens and a per-expert piece table
 //           (first rank t and destination base of every piece).
@@ -87,44 +90,54 @@ __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------- scan
-// Block: 64 experts (lanes) x 16 wavefronts, each wavefront a range of chunks.
+// Block (column group, partition): 64 experts (lanes) x 16 wavefronts of
+// kScanPart / 16 chunks each, one round of independent loads per wavefront.
+// counts[c][e] becomes the exclusive prefix over the partition's chunks before c;
+// part[p][e] the partition total.
+constexpr int kScanPerWave = kScanPart / 16;
+
 __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ counts, int nchunk,
-                                                         int E, int32_t* __restrict__ T) {
-  __shared__ int32_t part[16][64];
+                                                         int E, int32_t* __restrict__ part) {
+  __shared__ int32_t wsum[16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
-  const int per = (nchunk + 15) / 16;
-  const int c0 = w * per, c1 = min(nchunk, c0 + per);
+  const int c0 = blockIdx.y * kScanPart + w * kScanPerWave;
+  const bool col = e < E;
+  int v[kScanPerWave];
+#pragma unroll
+  for (int i = 0; i < kScanPerWave; ++i)
+    v[i] = (col && c0 + i < nchunk) ? counts[int64_t(c0 + i) * E + e] : 0;
   int s = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) s += counts[int64_t(c) * E + e];
-  part[w][lane] = s;
+#pragma unroll
+  for (int i = 0; i < kScanPerWave; ++i) {
+    const int x = v[i];
+    v[i] = s;
+    s += x;
+  }
+  wsum[w][lane] = s;
   __syncthreads();
   if (w == 0) {
     int run = 0;
     for (int i = 0; i < 16; ++i) {
-      const int v = part[i][lane];
-      part[i][lane] = run;
-      run += v;
+      const int x = wsum[i][lane];
+      wsum[i][lane] = run;
+      run += x;
     }
-    if (e < E) T[e] = run;
+    if (col) part[int64_t(blockIdx.y) * E + e] = run;
   }
   __syncthreads();
-  int run = part[w][lane];
-  if (e < E)
-    for (int c = c0; c < c1; ++c) {
-      const int64_t idx = int64_t(c) * E + e;
-      const int v = counts[idx];
-      counts[idx] = run;
-      run += v;
-    }
+  const int off = wsum[w][lane];
+#pragma unroll
+  for (int i = 0; i < kScanPerWave; ++i)
+    if (col && c0 + i < nchunk) counts[int64_t(c0 + i) * E + e] = off + v[i];
 }
 
 // ---------------------------------------------------------------- solve
 struct SolveArgs {
   int R, S, E, K, B, G, SK;
   int64_t NK;
-  const int32_t* T;
+  int32_t* part;      // [npart, E] partition totals -> exclusive prefix over partitions
+  int npart;
   int32_t* cu;        // [R, E+B+1]
   int32_t* replica;   // [R, B]
   int32_t* piece_ptr, *piece_tlo, *piece_base;
@@ -189,12 +202,24 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
   __shared__ unsigned long long s_total;
   if (tid == 0) s_total = 0;
   __syncthreads();
-  unsigned long long part = 0;
+  // T[e]: sum of the partition totals, which become the prefix over partitions
+  unsigned long long sum = 0;
   for (int e = tid; e < a.E; e += kSolveThreads) {
-    sm[L.T + e] = a.T[e];
-    part += a.T[e];
+    int run = 0;
+    for (int p0 = 0; p0 < a.npart; p0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = p0 + i < a.npart ? a.part[int64_t(p0 + i) * a.E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (p0 + i < a.npart) a.part[int64_t(p0 + i) * a.E + e] = run;
+        run += v[i];
+      }
+    }
+    sm[L.T + e] = run;
+    sum += run;
   }
-  atomicAdd(&s_total, part);
+  atomicAdd(&s_total, sum);
   for (int i = tid; i < a.R * EB; i += kSolveThreads) sm[L.rowlen + i] = 0;
   for (int i = tid; i < a.R * a.B; i += kSolveThreads) a.replica[i] = -1;
   __syncthreads();
@@ -224,11 +249,21 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
     sm[L.seq + p * a.G + pos] = e;
   }
   __syncthreads();
-  for (int e = tid; e < a.E; e += kSolveThreads) {
-    const int p = e / a.G, pe = sm[L.seqpos + e];
-    int off = 0;
-    for (int s = 0; s < pe; ++s) off += sm[L.T + sm[L.seq + p * a.G + s]];
-    sm[L.off + e] = off;
+  // off(e): T summed over the experts before e in its group's layout, one
+  // wavefront-wide exclusive scan per group and 64 layout positions
+  {
+    const int lane = tid & 63, w = tid >> 6;
+    for (int p = w; p < a.R; p += kSolveThreads / 64) {
+      int carry = 0;
+      for (int b = 0; b < a.G; b += 64) {
+        const int s = b + lane;
+        const int e = s < a.G ? sm[L.seq + p * a.G + s] : 0;
+        const int t = s < a.G ? sm[L.T + e] : 0;
+        const int incl = wave_incl_scan(t);
+        if (s < a.G) sm[L.off + e] = carry + incl - t;
+        carry += __shfl(incl, 63, 64);
+      }
+    }
   }
 
   // donor tree: sequential, R is small
@@ -368,7 +403,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
 // ---------------------------------------------------------------- assign
 __global__ __launch_bounds__(256) void plan_assign_kernel(
     const int32_t* __restrict__ topk, int N, int K, int E, int nchunk, int nbits,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ piece_ptr,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ part,
+    const int32_t* __restrict__ piece_ptr,
     const int32_t* __restrict__ piece_tlo, const int32_t* __restrict__ piece_base,
     const int32_t* __restrict__ flags, int32_t* __restrict__ slot_map,
     int32_t* __restrict__ src_index) {
@@ -387,7 +423,8 @@ __global__ __launch_bounds__(256) void plan_assign_kernel(
     return;
   }
   int32_t* run = lds + w * E;  // next rank of every expert inside this chunk
-  for (int e = lane; e < E; e += 64) run[e] = base[int64_t(c) * E + e];
+  const int32_t* pp = part + int64_t(c / kScanPart) * E;
+  for (int e = lane; e < E; e += 64) run[e] = base[int64_t(c) * E + e] + pp[e];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -443,7 +480,7 @@ extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, i
   const int N = s.R * s.S;
   const int nchunk = int(w.nchunk);
   int32_t* flags = ws_ptr<int32_t>(ws, w.flags);
-  int32_t* T = ws_ptr<int32_t>(ws, w.T);
+  int32_t* part = ws_ptr<int32_t>(ws, w.part);
   int32_t* counts = ws_ptr<int32_t>(ws, w.counts);
   int32_t* pptr = ws_ptr<int32_t>(ws, w.piece_ptr);
   int32_t* ptlo = ws_ptr<int32_t>(ws, w.piece_tlo);
@@ -456,13 +493,16 @@ extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, i
                                                               counts, flags);
     if (launch_status()) return MOONEP_EHIP;
   }
-  plan_scan_kernel<<<(s.E + 63) / 64, 1024, 0, strm>>>(counts, nchunk, s.E, T);
-  if (launch_status()) return MOONEP_EHIP;
+  if (nchunk > 0) {
+    plan_scan_kernel<<<dim3((s.E + 63) / 64, unsigned(w.npart)), 1024, 0, strm>>>(counts, nchunk,
+                                                                                  s.E, part);
+    if (launch_status()) return MOONEP_EHIP;
+  }
 
   SolveArgs a;
   a.R = s.R; a.S = s.S; a.E = s.E; a.K = s.K; a.B = s.B; a.G = s.E / s.R; a.SK = s.S * s.K;
   a.NK = int64_t(N) * s.K;
-  a.T = T; a.cu = cu_seqlens; a.replica = replica_expert;
+  a.part = part; a.npart = int(w.npart); a.cu = cu_seqlens; a.replica = replica_expert;
   a.piece_ptr = pptr; a.piece_tlo = ptlo; a.piece_base = pbase; a.flags = flags;
   const size_t solve_lds = size_t(SolveLds(s.R, s.E, s.B).total) * 4;
   if (solve_lds > 64 * 1024) return MOONEP_ELIMIT;
@@ -473,7 +513,7 @@ extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, i
     int nbits = 0;
     while ((1 << nbits) < s.E) ++nbits;
     plan_assign_kernel<<<chunk_blocks, 256, chunk_lds, strm>>>(
-        topk_idx, N, s.K, s.E, nchunk, nbits, counts, pptr, ptlo, pbase, flags, slot_map,
+        topk_idx, N, s.K, s.E, nchunk, nbits, counts, part, pptr, ptlo, pbase, flags, slot_map,
         src_index);
     if (launch_status()) return MOONEP_EHIP;
   }
