@@ -113,6 +113,7 @@ constexpr int kRsrcFlags = 0x00020000;      // raw (unswizzled) 32-bit data, gfx
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used here
 constexpr int kBK = 32;                     // k per pipeline step
 constexpr int kStages = 4;                  // LDS ring depth
+constexpr int kBlockE = 4, kBlockN = 8;     // FWD/DGRAD tile order block
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -258,7 +259,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   const int Kfix = OP == MOONEP_FWD ? g.H : g.Hp;     // FWD/DGRAD reduction length
   const int NT = (Ndim + BN - 1) / BN;
   const int MT = OP == MOONEP_WGRAD ? (g.H + BM - 1) / BM : 1;
-  const int64_t total = int64_t(*g.ntiles) * MT * NT;
+  const int64_t nent = *g.ntiles;
+  const int64_t total = nent * MT * NT;
   const int64_t wsz = int64_t(g.H) * g.Hp;
   const uint32_t lda_b = uint32_t(OP == MOONEP_DGRAD ? g.Hp : g.H) * 2;   // bytes per A row
   const uint32_t ldb_b = uint32_t(g.Hp) * 2;                              // bytes per B row
@@ -275,9 +277,26 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
   for (int64_t tau = slot; tau < total; tau += G) {
-    const int64_t ent = tau / (int64_t(MT) * NT);
-    const int rem = int(tau % (int64_t(MT) * NT));
-    const int mt = rem / NT, nt = rem % NT;
+    int64_t ent;
+    int mt, nt;
+    if (OP == MOONEP_WGRAD) {
+      ent = tau / (int64_t(MT) * NT);
+      const int rem = int(tau % (int64_t(MT) * NT));
+      mt = rem / NT;
+      nt = rem % NT;
+    } else {
+      // blocks of kBlockE entries x kBlockN N-tiles, so that the 32 concurrent tiles of
+      // an XCD reuse each weight N-tile for four M-tiles and each activation tile for
+      // eight N-tiles
+      const int64_t eb = tau / (int64_t(kBlockE) * NT);
+      const int j = int(tau % (int64_t(kBlockE) * NT));
+      const int ge = int(min(int64_t(kBlockE), nent - eb * kBlockE));
+      const int nb = j / (ge * kBlockN), jj = j % (ge * kBlockN);
+      const int wb = min(kBlockN, NT - nb * kBlockN);
+      ent = eb * kBlockE + jj / wb;
+      mt = 0;
+      nt = nb * kBlockN + jj % wb;
+    }
     const TileEntry te = g.tiles[ent];
     const int n0 = nt * BN;
     const int cols_valid = min(BN, Ndim - n0);
