@@ -282,3 +282,39 @@ def test_per_rank_subproblems_reproduce_the_full_gemm():
     assert torch.equal(layer1.out[layer1.slot_map.long()], layer.out[layer.slot_map.long()])
     pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
     assert rows == pl.L
+
+
+@pytest.mark.parametrize("kw", [
+    dict(R=4, S=40, E=1024, K=8, H=64, Hp=64),                 # largest expert count, B = 256
+    dict(R=2, S=53, E=8, K=1, H=320, Hp=192),                  # K = 1; H, H' end inside a tile
+    dict(R=2, S=24, E=64, K=32, H=64, Hp=128),                 # K = 32
+    dict(R=1, S=77, E=16, K=4, B=0, H=128, Hp=64, mode="infer"),   # one rank, no slots
+    dict(R=8, S=33, E=32, K=2, B=1, H=192, Hp=320, mode="infer"),  # overflow into home rows
+], ids=["E1024", "K1_ragged_tiles", "K32", "R1_B0", "infer_B1"])
+def test_edge_shapes_full_compare(kw):
+    """Forward (and backward where the layer trains) compared element by element with
+    the oracle at edge shapes of the plan and of the GEMM tiling."""
+    cfg = small_cfg(name="edge", **kw)
+    say("edge shape", kw)
+    alpha = 2.0 if cfg.E <= 64 else 4.0
+    bwd = cfg.mode == "train"
+    r, layer, d, topk, gates = _setup(cfg, 3.0, backward=bwd, alpha=alpha)
+    if bwd:
+        layer.grad_home.zero_()
+    _poison_forward(layer)
+    y = layer.forward(topk, d["x"], gates)
+    if bwd:
+        dx = layer.backward(d["dy"], gates)
+    torch.cuda.synchronize()
+    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    assert np.array_equal(layer.slot_map.cpu().numpy(), pl.slot_map)
+    assert np.array_equal(layer.cu_seqlens.cpu().numpy(), pl.cu_seqlens)
+    x_h, W_h = _host(d["x"]), _host(d["W"][:cfg.E])
+    y_ref = M.dense_forward(x_h, W_h, r.topk_idx, r.gates)
+    assert rel_err(_host(y), y_ref) <= tolerance(cfg)
+    if bwd:
+        dd = M.gated_dy(_host(d["dy"]), r.gates, cfg.dtype)
+        dx_ref, dW_ref = M.dense_backward(x_h, W_h, r.topk_idx, dd)
+        assert rel_err(_host(dx), dx_ref) <= tolerance(cfg)
+        assert rel_err(_host(layer.grad_home), dW_ref) <= tolerance(cfg)
+        assert int(torch.count_nonzero(layer.reduce_buf)) == 0
