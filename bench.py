@@ -11,7 +11,9 @@ shared seed. Inputs are resident in HBM before the timed region starts.
 Prints ONE JSON line (rank 0). Besides the contract fields:
   roofline      the grouped GEMM (dominant kernel) against dense bf16 MFMA peak;
                 its average duration comes from HIP events around every GEMM
-                launch inside the timed region, on the stream it runs on;
+                call inside the timed region, on the stream it runs on (one call
+                = the tile-list kernel, the 256x256-tile kernel and the
+                short-tail kernel); traffic = HBM bytes of both GEMM kernels;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
   stages_us     per-stage median microseconds at every imbalance point
                 (each repetition after a 1 GiB write that evicts the caches);
@@ -214,7 +216,8 @@ def main():
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(), "kernel": "gemm_bf16_kernel (FWD)",
+                "traffic": stored_traffic(),
+                "kernel": "moonep_grouped_gemm FWD: gemm_bf16_kernel 256x256 tiles + 128x512 tails",
                 "avg_launch_ms": round(gemm_ms, 4), "flop_per_launch": flops}
 
     out = {

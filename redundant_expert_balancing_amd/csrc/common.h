@@ -18,11 +18,14 @@ constexpr int kScanPart = 64;
 constexpr int kMinTileM = 64;
 
 // Sticky error word and per-call words at the head of the workspace.
-enum FlagWord { kFlagError = 0, kFlagPlanValid = 1, kFlagTileCount = 2, kFlagWords = 64 };
+enum FlagWord {
+  kFlagError = 0, kFlagPlanValid = 1, kFlagTileCount = 2, kFlagTileCountTail = 3,
+  kFlagWords = 64
+};
 
 struct WsLayout {
-  size_t flags, part, counts, piece_ptr, piece_tlo, piece_base, tiles, total;
-  int64_t nchunk, npart, max_pieces, max_tiles;
+  size_t flags, part, counts, piece_ptr, piece_tlo, piece_base, tiles, tiles_tail, total;
+  int64_t nchunk, npart, max_pieces, max_tiles, max_tail;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -35,6 +38,7 @@ inline WsLayout ws_layout(const moonep_shape& s) {
   w.npart = (w.nchunk + kScanPart - 1) / kScanPart;
   w.max_pieces = int64_t(s.E) + 2 * int64_t(s.R) + 8;
   w.max_tiles = int64_t(s.R) * ((SK + kMinTileM - 1) / kMinTileM + s.E + s.B) + 1;
+  w.max_tail = int64_t(s.R) * (s.E + s.B) + 1;   // at most one short tail per segment
   size_t o = 0;
   w.flags = o;      o = align256(o + kFlagWords * 4);
   w.part = o;       o = align256(o + size_t(w.npart) * s.E * 4);
@@ -43,6 +47,7 @@ inline WsLayout ws_layout(const moonep_shape& s) {
   w.piece_tlo = o;  o = align256(o + size_t(w.max_pieces) * 4);
   w.piece_base = o; o = align256(o + size_t(w.max_pieces) * 4);
   w.tiles = o;      o = align256(o + size_t(w.max_tiles) * 16);
+  w.tiles_tail = o; o = align256(o + size_t(w.max_tail) * 16);
   w.total = o;
   return w;
 }

@@ -51,46 +51,79 @@ __device__ inline int wave_scan_incl(int v) {
   return v;
 }
 
+// M-tiles of bm rows per segment (bm = 0: one entry per whole segment). With
+// tail > 0 a segment's last M-tile goes to a second list when it has at most
+// `tail` rows: those are computed by a kernel with tail-row M-tiles and twice
+// the N width, so a short tail costs half as many MFMAs.
 __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restrict__ cu, int R,
-                                                          int E, int B, int SK, int bm,
+                                                          int E, int B, int SK, int bm, int tail,
                                                           TileEntry* __restrict__ tiles,
                                                           int32_t* __restrict__ ntiles,
-                                                          int max_tiles) {
-  __shared__ int swave[17];
+                                                          int max_tiles,
+                                                          TileEntry* __restrict__ tails,
+                                                          int32_t* __restrict__ ntails,
+                                                          int max_tails) {
+  __shared__ int swave[2][17];
   const int EB = E + B, total = R * EB;
   const int per = (total + 1023) / 1024;
   const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
-  int cnt = 0;
+  // full tiles of a segment of n rows, and whether its tail goes to the second list
+  auto split = [&](int n, int& nfull, int& ntail) {
+    if (bm <= 0) { nfull = 1; ntail = 0; return; }
+    nfull = (n + bm - 1) / bm;
+    const int rem = n - (nfull - 1) * bm;
+    ntail = (tail > 0 && rem <= tail) ? 1 : 0;
+    nfull -= ntail;
+  };
+  int cnt = 0, cnt_tail = 0;
   for (int idx = i0; idx < i1; ++idx) {
     const int q = idx / EB, i = idx % EB;
     const int n = cu[q * (EB + 1) + i + 1] - cu[q * (EB + 1) + i];
-    if (n > 0) cnt += bm > 0 ? (n + bm - 1) / bm : 1;
+    if (n <= 0) continue;
+    int f, t;
+    split(n, f, t);
+    cnt += f;
+    cnt_tail += t;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int incl = wave_scan_incl(cnt);
-  if (lane == 63) swave[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    const int x = lane < 16 ? swave[lane] : 0;
-    const int xi = wave_scan_incl(x);
-    if (lane < 16) swave[lane] = xi - x;
-    if (lane == 15) swave[16] = xi;
+  const int incl_t = wave_scan_incl(cnt_tail);
+  if (lane == 63) {
+    swave[0][w] = incl;
+    swave[1][w] = incl_t;
   }
   __syncthreads();
-  int k = swave[w] + incl - cnt;
+  if (w < 2) {
+    const int x = lane < 16 ? swave[w][lane] : 0;
+    const int xi = wave_scan_incl(x);
+    if (lane < 16) swave[w][lane] = xi - x;
+    if (lane == 15) swave[w][16] = xi;
+  }
+  __syncthreads();
+  int k = swave[0][w] + incl - cnt;
+  int kt = swave[1][w] + incl_t - cnt_tail;
   for (int idx = i0; idx < i1; ++idx) {
     const int q = idx / EB, i = idx % EB;
     const int c0 = cu[q * (EB + 1) + i];
     const int n = cu[q * (EB + 1) + i + 1] - c0;
     if (n <= 0) continue;
     const int wrow = i < E ? i : E + q * B + (i - E);
+    int f, t;
+    split(n, f, t);
     const int step = bm > 0 ? bm : n;
-    for (int m0 = 0; m0 < n; m0 += step) {
-      if (k < max_tiles) tiles[k] = TileEntry{q * SK + c0, wrow, m0, n};
+    for (int j = 0; j < f; ++j) {
+      if (k < max_tiles) tiles[k] = TileEntry{q * SK + c0, wrow, j * step, n};
       ++k;
     }
+    if (t) {
+      if (kt < max_tails) tails[kt] = TileEntry{q * SK + c0, wrow, f * step, n};
+      ++kt;
+    }
   }
-  if (threadIdx.x == 0) *ntiles = min(swave[16], max_tiles);
+  if (threadIdx.x == 0) {
+    *ntiles = min(swave[0][16], max_tiles);
+    *ntails = min(swave[1][16], max_tails);
+  }
 }
 
 // ------------------------------------------------------------------ staging
@@ -582,16 +615,34 @@ static int device_cus() {
 // a 4-stage LDS ring (128 KiB), one workgroup per CU. Four wavefronts of 128 x 128
 // (a third fewer LDS bytes per flop) measured 5% slower: one wavefront per SIMD
 // leaves every barrier exposed.
-template <int OP>
 struct TileCfg {
-  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, PER_CU = 1;
+  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4;
 };
+// Segment tails of at most kTailRows rows (FWD, DGRAD): 128 x 512 tiles, the same
+// 128 x 64 wavefront tile with the 8 wavefronts side by side in N, a 160 KiB ring.
+// A 256 x 256 tile spends as many MFMAs on a tail of 1..128 rows as on a full one;
+// a 128 x 512 tile covers twice the columns for the same MFMAs.
+struct TailCfg {
+  static constexpr int BM = 128, BN = 512, WAVES_M = 1, WAVES_N = 8;
+};
+constexpr int kTailRows = TailCfg::BM;
 
-template <int OP, bool SWIGLU = false>
-static void launch_bf16(const GemmArgs& g, int cus, hipStream_t strm) {
-  using C = TileCfg<OP>;
+template <int OP, bool SWIGLU, typename C>
+static void launch_cfg(const GemmArgs& g, int cus, hipStream_t strm) {
   gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU>
-      <<<cus * C::PER_CU, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
+      <<<cus, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
+}
+
+// the full-tile list, then (FWD and DGRAD) the tail list on the tail kernel
+template <int OP, bool SWIGLU = false>
+static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntails, int cus,
+                        hipStream_t strm) {
+  launch_cfg<OP, SWIGLU, TileCfg>(g, cus, strm);
+  if constexpr (OP != MOONEP_WGRAD) {
+    g.tiles = tails;
+    g.ntiles = ntails;
+    launch_cfg<OP, SWIGLU, TailCfg>(g, cus, strm);
+  }
 }
 
 }  // namespace moonep
@@ -620,11 +671,15 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
   }
   hipStream_t strm = as_stream(stream);
   TileEntry* tiles = ws_ptr<TileEntry>(ws, w.tiles);
+  TileEntry* tails = ws_ptr<TileEntry>(ws, w.tiles_tail);
   int32_t* ntiles = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount;
+  int32_t* ntails = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail;
   const bool bf16 = s.dtype == MOONEP_BF16;
-  const int bm = (op == MOONEP_WGRAD || !bf16) ? 0 : TileCfg<MOONEP_FWD>::BM;
-  gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K, bm, tiles, ntiles,
-                                          int(w.max_tiles));
+  const bool mtiled = bf16 && op != MOONEP_WGRAD;
+  gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
+                                          mtiled ? TileCfg::BM : 0, mtiled ? kTailRows : 0,
+                                          tiles, ntiles, int(w.max_tiles), tails, ntails,
+                                          int(w.max_tail));
   if (launch_status()) return MOONEP_EHIP;
 
   if (bf16) {
@@ -632,9 +687,9 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
     if (cus <= 0) return MOONEP_EHIP;
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
                reduce_buf, tiles, ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
-    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, cus, strm);
-    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, cus, strm);
-    else launch_bf16<MOONEP_WGRAD>(g, cus, strm);
+    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, tails, ntails, cus, strm);
+    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, tails, ntails, cus, strm);
+    else launch_bf16<MOONEP_WGRAD>(g, tails, ntails, cus, strm);
   } else {
     const dim3 grid(64, 256);
     const float* af = static_cast<const float*>(a);
@@ -664,11 +719,14 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
   if (h_saved && !aligned16(h_saved)) return MOONEP_EINVAL;
   hipStream_t strm = as_stream(stream);
   TileEntry* tiles = ws_ptr<TileEntry>(ws, w.tiles);
+  TileEntry* tails = ws_ptr<TileEntry>(ws, w.tiles_tail);
   int32_t* ntiles = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount;
+  int32_t* ntails = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail;
   const bool bf16 = s.dtype == MOONEP_BF16;
-  const int bm = bf16 ? TileCfg<MOONEP_FWD>::BM : 0;
-  gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K, bm, tiles, ntiles,
-                                          int(w.max_tiles));
+  gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
+                                          bf16 ? TileCfg::BM : 0, bf16 ? kTailRows : 0, tiles,
+                                          ntiles, int(w.max_tiles), tails, ntails,
+                                          int(w.max_tail));
   if (launch_status()) return MOONEP_EHIP;
   if (bf16) {
     const int cus = device_cus();
@@ -676,7 +734,7 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
     GemmArgs g{static_cast<const uint16_t*>(xp), static_cast<const uint16_t*>(w1_all), nullptr,
                nullptr, nullptr, tiles, ntiles, s.H, 2 * s.Hp, s.E,
                static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved)};
-    launch_bf16<MOONEP_FWD, true>(g, cus, strm);
+    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, cus, strm);
   } else {
     gemm_fp32_swiglu_kernel<<<dim3(64, 256), 256, 0, strm>>>(
         static_cast<const float*>(xp), static_cast<const float*>(w1_all),
