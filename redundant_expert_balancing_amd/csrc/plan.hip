@@ -401,21 +401,38 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
 }
 
 // ---------------------------------------------------------------- assign
+// The piece table is staged in LDS by the workgroup; each wavefront loads the ids
+// of 8 steps at once, so a step waits on no global load.
+constexpr int kAssignBatch = 8;
+
 __global__ __launch_bounds__(256) void plan_assign_kernel(
     const int32_t* __restrict__ topk, int N, int K, int E, int nchunk, int nbits,
     const int32_t* __restrict__ base, const int32_t* __restrict__ part,
-    const int32_t* __restrict__ piece_ptr,
-    const int32_t* __restrict__ piece_tlo, const int32_t* __restrict__ piece_base,
-    const int32_t* __restrict__ flags, int32_t* __restrict__ slot_map,
-    int32_t* __restrict__ src_index) {
+    const int32_t* __restrict__ piece_ptr, const int32_t* __restrict__ piece_tlo,
+    const int32_t* __restrict__ piece_base, int max_pieces, const int32_t* __restrict__ flags,
+    int32_t* __restrict__ slot_map, int32_t* __restrict__ src_index) {
+  // LDS: run[kWavesPerBlock][E] | ptr[E+1] | tlo[max_pieces] | pbase[max_pieces]
   extern __shared__ int32_t lds[];
+  int32_t* s_ptr = lds + kWavesPerBlock * E;
+  int32_t* s_tlo = s_ptr + E + 1;
+  int32_t* s_base = s_tlo + max_pieces;
+  const bool valid = flags[kFlagPlanValid] != 0;
+  if (valid) {
+    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_ptr[i] = piece_ptr[i];
+    const int np = min(piece_ptr[E], max_pieces);
+    for (int i = threadIdx.x; i < np; i += blockDim.x) {
+      s_tlo[i] = piece_tlo[i];
+      s_base[i] = piece_base[i];
+    }
+  }
+  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * kWavesPerBlock + w;
   if (c >= nchunk) return;  // whole wavefront leaves; no block barrier follows
   const int64_t NK = int64_t(N) * K;
   const int64_t u0 = int64_t(c) * kChunkTokens * K;
   const int64_t u1 = min(NK, u0 + int64_t(kChunkTokens) * K);
-  if (flags[kFlagPlanValid] == 0) {
+  if (!valid) {
     for (int64_t u = u0 + lane; u < u1; u += 64) {
       slot_map[u] = -1;
       src_index[u] = -1;
@@ -430,30 +447,42 @@ __global__ __launch_bounds__(256) void plan_assign_kernel(
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  for (int64_t s = u0; s < u1; s += 64) {
-    const int64_t u = s + lane;
-    const bool act = u < u1;
-    const int v = act ? topk[u] : 0;
-    // lanes holding the same expert id: intersect the ballots of every id bit
-    uint64_t m = __ballot(act);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (v >> b) & 1;
-      const uint64_t bal = __ballot(act && bit);
-      m &= bit ? bal : ~bal;
+  const int nsteps = int((u1 - u0 + 63) / 64);
+  for (int s0 = 0; s0 < nsteps; s0 += kAssignBatch) {
+    int vv[kAssignBatch];
+#pragma unroll
+    for (int j = 0; j < kAssignBatch; ++j) {
+      const int64_t u = u0 + int64_t(s0 + j) * 64 + lane;
+      vv[j] = u < u1 ? topk[u] : 0;
     }
-    int old = 0;
-    const uint64_t below = m & lt_mask;
-    if (act && below == 0) old = atomicAdd(&run[v], __popcll(m));  // group leader
-    const int leader = act ? __ffsll((unsigned long long)m) - 1 : lane;
-    const int grp_base = __shfl(old, leader, 64);
-    if (act) {
-      const int t = grp_base + __popcll(below);
-      int p = piece_ptr[v];
-      const int p1 = piece_ptr[v + 1];
-      while (p + 1 < p1 && piece_tlo[p + 1] <= t) ++p;
-      const int dest = p < p1 ? piece_base[p] + t : -1;
-      slot_map[u] = dest;
-      if (dest >= 0 && int64_t(dest) < NK) src_index[dest] = int32_t(u);
+#pragma unroll
+    for (int j = 0; j < kAssignBatch; ++j) {
+      if (s0 + j < nsteps) {
+        const int64_t u = u0 + int64_t(s0 + j) * 64 + lane;
+        const bool act = u < u1;
+        const int v = vv[j];
+        // lanes holding the same expert id: intersect the ballots of every id bit
+        uint64_t m = __ballot(act);
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = (v >> b) & 1;
+          const uint64_t bal = __ballot(act && bit);
+          m &= bit ? bal : ~bal;
+        }
+        int old = 0;
+        const uint64_t below = m & lt_mask;
+        if (act && below == 0) old = atomicAdd(&run[v], __popcll(m));  // group leader
+        const int leader = act ? __ffsll((unsigned long long)m) - 1 : lane;
+        const int grp_base = __shfl(old, leader, 64);
+        if (act) {
+          const int t = grp_base + __popcll(below);
+          int p = s_ptr[v];
+          const int p1 = s_ptr[v + 1];
+          while (p + 1 < p1 && s_tlo[p + 1] <= t) ++p;
+          const int dest = p < p1 ? s_base[p] + t : -1;
+          slot_map[u] = dest;
+          if (dest >= 0 && int64_t(dest) < NK) src_index[dest] = int32_t(u);
+        }
+      }
     }
   }
 }
@@ -512,8 +541,10 @@ extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, i
   if (nchunk > 0) {
     int nbits = 0;
     while ((1 << nbits) < s.E) ++nbits;
-    plan_assign_kernel<<<chunk_blocks, 256, chunk_lds, strm>>>(
-        topk_idx, N, s.K, s.E, nchunk, nbits, counts, part, pptr, ptlo, pbase, flags, slot_map,
+    const size_t assign_lds = chunk_lds + (size_t(s.E) + 1 + 2 * size_t(w.max_pieces)) * 4;
+    plan_assign_kernel<<<chunk_blocks, 256, assign_lds, strm>>>(
+        topk_idx, N, s.K, s.E, nchunk, nbits, counts, part, pptr, ptlo, pbase,
+        int(w.max_pieces), flags, slot_map,
         src_index);
     if (launch_status()) return MOONEP_EHIP;
   }
