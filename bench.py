@@ -119,8 +119,14 @@ def cpu_baseline(cfg, routing, x_dev, w_dev, n_tok: int = 24):
     M.dense_forward(x_s, Wmap(), routing.topk_idx[toks], routing.gates[toks])
     t_dense = time.perf_counter() - t0
     per_token = t_plan / cfg.N + t_dense / n_tok
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(1.0 / per_token, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu,
             "sample": (f"plan rule on the full {cfg.N}-token routing at maxvio "
                        f"{routing.maxvio:.3g} ({t_plan:.2f} s, 1 thread) + float64 dense "
                        f"projection and gated combine of {n_tok} sampled tokens "
@@ -283,6 +289,10 @@ def stage_table(cfg, layer, x, topks, gates, routings, reps):
                 ts.append(a.elapsed_time(b) * 1e3)
             row[name] = round(float(np.median(ts)), 1)
         row["replicas"] = int((layer.replica_expert[:, :cfg.B] >= 0).sum())
+        # the skew the plan removes: the hottest rank's home load over S*K
+        T = np.bincount(r.topk_idx.ravel(), minlength=cfg.E)
+        row["max_home_load_over_SK"] = round(float(T.reshape(cfg.R, cfg.G).sum(1).max())
+                                             / (cfg.S * cfg.K), 4)
         table[f"maxvio={r.maxvio:.3g}"] = row
     N, K, H, Hp = cfg.N, cfg.K, cfg.H, cfg.Hp
     plan_b = 12 * N * K + 4 * cfg.R * (cfg.E + cfg.B + 1)
