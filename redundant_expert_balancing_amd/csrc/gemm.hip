@@ -2,12 +2,17 @@
 //
 // Experts are addressed purely by row index and the active rows come only from
 // cu_seqlens, which never leaves the device [ai-maestro.online "Moonshot AI
-// open-sources MoonEP", section "The memory contract"]. Two launches per call:
+// open-sources MoonEP", section "The memory contract"]. Launches per call:
 //
-//   tiles   one workgroup turns cu_seqlens [R, E+B+1] into a compact list of
-//           work entries (segment start row, weight row, M offset, length).
-//   gemm    a persistent kernel walks entry x N-tile (x M-tile for WGRAD) in an
-//           order that keeps the workgroups of one XCD on neighbouring tiles.
+//   tiles   one workgroup turns cu_seqlens [R, E+B+1] into compact lists of work
+//           entries (segment start row, weight row, M offset, length): 256-row
+//           M-tiles, and (FWD, DGRAD) a second list of segment tails of at most
+//           128 rows.
+//   gemm    a persistent kernel walks entry x N-tile (x M-tile for WGRAD) with
+//           256 x 256 tiles; the 32 concurrent tiles of one XCD form a block of 4
+//           entries x 8 N-tiles, so they share operand slices in that XCD's L2.
+//   tails   (FWD, DGRAD) the same kernel with 128 x 512 tiles over the tail list:
+//           half the MFMAs a 256 x 256 tile spends on a tail of 1..128 rows.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation; operands go
 // global -> LDS by DMA into a ring of k-steps; operands stored with M or N
