@@ -146,8 +146,8 @@ struct SolveArgs {
 
 // LDS carve-up of the solve kernel (ints).
 struct SolveLds {
-  int T, seqpos, off, seq, npiece, hot, parent, L, gchild, gamt, gdonor, glo, gfirst, dptr,
-      dfill, homestart, rowlen, swave, misc, total;
+  int T, seqpos, off, seq, npiece, hot, hsum, crank, csum, cdon, cfirst, clast, chain, L, gchild,
+      gamt, glo, gfirst, dptr, homestart, rowlen, swave, misc, total;
   __host__ __device__ SolveLds(int R, int E, int B) {
     int o = 0;
     T = o; o += E;
@@ -155,16 +155,20 @@ struct SolveLds {
     off = o; o += E;
     seq = o; o += E;
     npiece = o; o += E;
-    hot = o; o += R;
-    parent = o; o += R;
+    hot = o; o += R;      // hot ranks in ascending id
+    hsum = o; o += R;     // their excess, inclusive prefix
+    crank = o; o += R;    // cold ranks in ascending id
+    csum = o; o += R;     // their need, inclusive prefix
+    cdon = o; o += R;     // hot index each cold rank takes from
+    cfirst = o; o += R;   // per hot index: first and last cold index it gives to
+    clast = o; o += R;
+    chain = o; o += R;    // per hot index: what it passes to the previous hot rank
     L = o; o += R;
     gchild = o; o += R;
     gamt = o; o += R;
-    gdonor = o; o += R;
     glo = o; o += R;
     gfirst = o; o += R;
     dptr = o; o += R + 1;
-    dfill = o; o += R;
     homestart = o; o += R;
     rowlen = o; o += R * (E + B);
     swave = o; o += kSolveThreads / 64 + 1;
@@ -266,68 +270,111 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
     }
   }
 
-  // donor tree: sequential, R is small
-  if (tid == 0) {
-    int nhot = 0, ngift = 0;
-    for (int p = 0; p < a.R; ++p) {
-      sm[L.parent + p] = -1;
-      if (sm[L.L + p] > a.SK) sm[L.hot + nhot++] = p;
+  // Donor tree, in closed form. The rule (moonep_plan) walks the cold ranks in
+  // ascending id; a receiver takes all it lacks from the current donor, a donor
+  // that runs short takes the deficit from the next hot rank. With S_i the hot
+  // ranks' excess summed in ascending id (inclusive) and D_j the cold ranks' need
+  // likewise, the donor's running surplus before cold j is S_i - D_(j-1), so:
+  //   cold j takes from hot i(j) = min{ i : S_i > D_(j-1) };
+  //   hot i gives D_j - S_(i-1) to hot i-1 exactly when D_(j-1) < S_(i-1) < D_j,
+  //   and that gift is made before any of hot i's gifts to cold ranks.
+  // A donor's gift list is therefore its gift to the previous hot rank (if any),
+  // then its cold ranks in ascending id; consecutive layout ranges from 0 follow.
+  {
+    const int p = tid;
+    const bool in = p < a.R;
+    const int lp = in ? sm[L.L + p] : 0;
+    const int ishot = in && lp > a.SK, iscold = in && lp < a.SK;
+    int nhot, ncold, sx, sn;
+    const int hidx = block_excl_scan(ishot, sm + L.swave, &nhot);
+    const int cidx = block_excl_scan(iscold, sm + L.swave, &ncold);
+    const int hpre = block_excl_scan(ishot ? lp - a.SK : 0, sm + L.swave, &sx);
+    const int cpre = block_excl_scan(iscold ? a.SK - lp : 0, sm + L.swave, &sn);
+    if (ishot) {
+      sm[L.hot + hidx] = p;
+      sm[L.hsum + hidx] = hpre + (lp - a.SK);
+      sm[L.cfirst + hidx] = -1;
+      sm[L.clast + hidx] = -2;
     }
-    if (nhot > 0) {
-      int i = 0;
-      int avail = sm[L.L + sm[L.hot]] - a.SK;
-      for (int q = 0; q < a.R; ++q) {
-        const int lq = sm[L.L + q];
-        if (lq >= a.SK) continue;
-        const int need = a.SK - lq;
-        const int d = sm[L.hot + i];
-        sm[L.parent + q] = d;
-        sm[L.gdonor + ngift] = d; sm[L.gchild + ngift] = q; sm[L.gamt + ngift] = need; ++ngift;
-        avail -= need;
-        while (avail < 0 && i + 1 < nhot) {
-          const int cur = sm[L.hot + i], nxt = sm[L.hot + i + 1];
-          sm[L.parent + cur] = nxt;
-          sm[L.gdonor + ngift] = nxt; sm[L.gchild + ngift] = cur; sm[L.gamt + ngift] = -avail; ++ngift;
-          avail += sm[L.L + nxt] - a.SK;
-          ++i;
+    if (iscold) {
+      sm[L.crank + cidx] = p;
+      sm[L.csum + cidx] = cpre + (a.SK - lp);
+    }
+    __syncthreads();
+    // cold j: its donor's hot index, by binary search over S
+    if (tid < ncold) {
+      const int dprev = tid > 0 ? sm[L.csum + tid - 1] : 0;
+      int lo = 0, hi = nhot - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sm[L.hsum + mid] > dprev) hi = mid; else lo = mid + 1;
+      }
+      sm[L.cdon + tid] = lo;
+    }
+    // hot i >= 1: the gift to hot i-1, by binary search over D
+    if (tid < nhot) {
+      int amt = 0;
+      if (tid > 0) {
+        const int sp = sm[L.hsum + tid - 1];
+        int lo = 0, hi = ncold;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (sm[L.csum + mid] > sp) hi = mid; else lo = mid + 1;
         }
-        if (avail == 0 && i + 1 < nhot) {
-          ++i;
-          avail = sm[L.L + sm[L.hot + i]] - a.SK;
+        const int dprev = lo > 0 ? sm[L.csum + lo - 1] : 0;
+        if (lo < ncold && dprev < sp) amt = sm[L.csum + lo] - sp;
+      }
+      sm[L.chain + tid] = amt;
+    }
+    __syncthreads();
+    // the run of cold ranks each donor gives to (cdon is non-decreasing in j)
+    if (tid < ncold) {
+      const int d = sm[L.cdon + tid];
+      if (tid == 0 || sm[L.cdon + tid - 1] != d) sm[L.cfirst + d] = tid;
+      if (tid == ncold - 1 || sm[L.cdon + tid + 1] != d) sm[L.clast + d] = tid;
+    }
+    __syncthreads();
+    // gift counts per donor rank, grouped by donor in ascending id
+    int cnt = 0, chain_amt = 0, first = -1, last = -2;
+    if (ishot) {
+      chain_amt = sm[L.chain + hidx];
+      first = sm[L.cfirst + hidx];
+      last = sm[L.clast + hidx];
+      cnt = (chain_amt > 0) + (last - first + 1);
+    }
+    int ngift;
+    const int base = block_excl_scan(cnt, sm + L.swave, &ngift);
+    if (in) sm[L.dptr + p] = base;
+    if (tid == 0) {
+      sm[L.dptr + a.R] = ngift;
+      sm[L.misc] = ngift;
+    }
+    if (in) {
+      int given = 0;
+      if (ishot) {
+        const int d0 = first > 0 ? sm[L.csum + first - 1] : 0;
+        given = chain_amt + (last >= first ? sm[L.csum + last] - d0 : 0);
+        if (chain_amt > 0) {
+          sm[L.gchild + base] = sm[L.hot + hidx - 1];
+          sm[L.gamt + base] = chain_amt;
+          sm[L.glo + base] = 0;
         }
       }
+      sm[L.homestart + p] = given;
     }
-    // group the gifts by donor, keeping the order they were made in
-    for (int p = 0; p <= a.R; ++p) sm[L.dptr + p] = 0;
-    for (int k = 0; k < ngift; ++k) sm[L.dptr + sm[L.gdonor + k] + 1]++;
-    for (int p = 0; p < a.R; ++p) sm[L.dptr + p + 1] += sm[L.dptr + p];
-    for (int p = 0; p < a.R; ++p) {
-      sm[L.dfill + p] = sm[L.dptr + p];
-      sm[L.homestart + p] = 0;
+    __syncthreads();
+    if (tid < ncold) {
+      const int i = sm[L.cdon + tid];
+      const int d = sm[L.hot + i];
+      const int ch = sm[L.chain + i];
+      const int first_j = sm[L.cfirst + i];
+      const int k = sm[L.dptr + d] + (ch > 0) + (tid - first_j);
+      const int dprev = tid > 0 ? sm[L.csum + tid - 1] : 0;
+      const int dfirst = first_j > 0 ? sm[L.csum + first_j - 1] : 0;
+      sm[L.gchild + k] = sm[L.crank + tid];
+      sm[L.gamt + k] = sm[L.csum + tid] - dprev;
+      sm[L.glo + k] = ch + (dprev - dfirst);
     }
-    // second pass writes sorted copies after the raw lists (gfirst used as scratch)
-    int* child = sm + L.gfirst;  // temporary: child, reused below
-    int* amt = sm + L.glo;       // temporary: amount
-    for (int k = 0; k < ngift; ++k) {
-      const int d = sm[L.gdonor + k];
-      const int slot = sm[L.dfill + d]++;
-      child[slot] = sm[L.gchild + k];
-      amt[slot] = sm[L.gamt + k];
-    }
-    for (int k = 0; k < ngift; ++k) {
-      sm[L.gchild + k] = child[k];
-      sm[L.gamt + k] = amt[k];
-    }
-    // consecutive ranges of the donor's layout, starting at 0, in gift order
-    for (int p = 0; p < a.R; ++p) {
-      int start = 0;
-      for (int k = sm[L.dptr + p]; k < sm[L.dptr + p + 1]; ++k) {
-        sm[L.glo + k] = start;
-        start += sm[L.gamt + k];
-      }
-      sm[L.homestart + p] = start;
-    }
-    sm[L.misc] = ngift;
   }
   __syncthreads();
 
