@@ -295,7 +295,9 @@ int moonep_pool_create(const moonep_shape* shape, int32_t nsets, moonep_pool** p
 /* Physical bytes the pool holds (all sets). */
 size_t moonep_pool_bytes(const moonep_pool* pool);
 
-/* Release the pool. Every view on it must be destroyed first. */
+/* Release the pool's physical memory. Destroy every view on it first (releasing a
+ * pool whose slots are still mapped is not supported); destroying a view never
+ * reads the pool. */
 int moonep_pool_destroy(moonep_pool* pool);
 
 /* A layer's [E+R*B, H, Hp] view: fresh home rows plus slot set `set` of `pool`.

@@ -29,11 +29,11 @@ struct moonep_pool {
 };
 
 struct moonep_view {
-  moonep_pool* pool;
   int32_t set;
   void* va;
   size_t va_bytes;
   size_t home_bytes;
+  size_t slot_bytes;   // a copy: destroying the view never reads the pool
   hipMemGenericAllocationHandle_t home;
 };
 
@@ -145,9 +145,9 @@ extern "C" int moonep_view_create(const moonep_shape* shape, moonep_pool* pool, 
   if (home_bytes == 0 || home_bytes % pool->gran) return MOONEP_EINVAL;
   moonep_view* v = new (std::nothrow) moonep_view{};
   if (!v) return MOONEP_EHIP;
-  v->pool = pool;
   v->set = set;
   v->home_bytes = home_bytes;
+  v->slot_bytes = pool->set_bytes;
   v->va_bytes = home_bytes + pool->set_bytes;
   const hipMemAllocationProp prop = device_prop(dev);
   bool reserved = false, created = false, home_mapped = false, slots_mapped = false;
@@ -184,7 +184,7 @@ extern "C" int moonep_view_destroy(moonep_view* view) {
   // no kernel may still read the range being unmapped
   int st = hipDeviceSynchronize() == hipSuccess ? MOONEP_OK : MOONEP_EHIP;
   char* va = static_cast<char*>(view->va);
-  if (hipMemUnmap(va + view->home_bytes, view->pool->set_bytes) != hipSuccess) st = MOONEP_EHIP;
+  if (hipMemUnmap(va + view->home_bytes, view->slot_bytes) != hipSuccess) st = MOONEP_EHIP;
   if (hipMemUnmap(va, view->home_bytes) != hipSuccess) st = MOONEP_EHIP;
   if (hipMemRelease(view->home) != hipSuccess) st = MOONEP_EHIP;
   if (hipMemAddressFree(view->va, view->va_bytes) != hipSuccess) st = MOONEP_EHIP;
