@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--config", default="bench_shape")
-    ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--stage-reps", type=int, default=50,
+                    help="timed repetitions per stage in the stage table (after 5 warm-ups)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -249,14 +250,17 @@ def main():
     if not args.no_stages:
         out["stages_us"], out["hbm_stages"] = stage_table(cfg, layer, x, topks, gates, routings,
                                                           args.stage_reps)
+        out["tokens_per_s_excluding_prefetch"] = tokens_excluding_prefetch(cfg, out["stages_us"])
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, routings[-1], x, d["W"])
     print(json.dumps(out), flush=True)
 
 
-def stage_table(cfg, layer, x, topks, gates, routings, reps):
-    """Median microseconds of each stage per imbalance point, caches flushed."""
+def stage_table(cfg, layer, x, topks, gates, routings, reps, warm=5):
+    """Median (and minimum, key suffix _min) microseconds of each stage per imbalance
+    point over `reps` repetitions after `warm` untimed ones, each repetition after a
+    1 GiB write that evicts the caches."""
     import numpy as np
     import torch
 
@@ -277,6 +281,8 @@ def stage_table(cfg, layer, x, topks, gates, routings, reps):
         layer.gemm_fwd()
         row = {}
         for name, fn in stages.items():
+            for _ in range(warm):
+                fn(j)
             ts = []
             for _ in range(reps):
                 flush.fill_(1.0)
@@ -288,6 +294,7 @@ def stage_table(cfg, layer, x, topks, gates, routings, reps):
                 torch.cuda.synchronize()
                 ts.append(a.elapsed_time(b) * 1e3)
             row[name] = round(float(np.median(ts)), 1)
+            row[name + "_min"] = round(float(np.min(ts)), 1)
         row["replicas"] = int((layer.replica_expert[:, :cfg.B] >= 0).sum())
         # the skew the plan removes: the hottest rank's home load over S*K
         T = np.bincount(r.topk_idx.ravel(), minlength=cfg.E)
@@ -303,6 +310,16 @@ def stage_table(cfg, layer, x, topks, gates, routings, reps):
     hbm = {"bytes": plan_b + disp_b + comb_b, "us": round(t, 1), "achieved": round(gbs, 1),
            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     return table, hbm
+
+
+def tokens_excluding_prefetch(cfg, table):
+    """The second figure of the metric: R*S / (plan + dispatch + GEMM + combine), stage
+    medians averaged over the imbalance points (prefetch scales with the replica count
+    by construction and is left out)."""
+    import numpy as np
+    t = float(np.mean([v["plan"] + v["dispatch"] + v["gemm"] + v["combine"]
+                       for v in table.values()]))
+    return round(cfg.N / (t * 1e-6), 1)
 
 
 def all_configs_table(reps):
