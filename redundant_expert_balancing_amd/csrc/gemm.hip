@@ -17,11 +17,12 @@
 // bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation; operands go
 // global -> LDS by DMA into a ring of k-steps; operands stored with M or N
 // contiguous (the weight in FWD, both operands in WGRAD) stay untransposed in
-// LDS and are read with the gfx950 transposing LDS read. Each wavefront holds the
-// fragments of the step it multiplies in registers and refills them from the
-// next step right behind its MFMAs (one LDS read between consecutive MFMAs), so
-// the per-step barrier does not drain the MFMA pipe and a ring stage is free one
-// step earlier: the DMAs run three steps ahead in a four-stage ring.
+// LDS and are read with the gfx950 transposing LDS read. A k-step is 64 deep, so
+// every DMA of a k-contiguous operand moves whole 128-byte lines. Each wavefront
+// holds the fragments of half a step in registers and refills them right behind
+// its MFMAs (one LDS read between consecutive MFMAs); the one barrier per step
+// sits after the last reads of the step's stage, so a two-stage ring keeps the
+// DMAs one step ahead and the MFMA pipe never drains at the barrier.
 // fp32 path: a plain FMA kernel per output element (tiny layers only).
 //
 // The gate/up projection of the expert FFN can run with its SwiGLU fused into the
@@ -139,23 +140,27 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
 // tiles therefore need no branches. No operand passes through registers, so
 // the k-loop keeps several steps in flight in a ring of LDS stages.
 //
-// LDS layouts of one 32-deep k-step (16-byte chunks XOR-swizzled so that the
+// LDS layouts of one 64-deep k-step (16-byte chunks XOR-swizzled so that the
 // fragment reads of 8 or 16 lanes at a time hit distinct banks):
-//   k-contiguous operand   [ROWS][32]: 64-byte rows, chunk c of row r at c ^ swz_k(r)
-//   m/n-contiguous operand [32][COLS]: one row per k, chunk c of row k at c ^ swz_mn(k);
+//   k-contiguous operand   [ROWS][64]: 128-byte rows, chunk c of row r at c ^ swz_k(r).
+//     One DMA instruction moves 8 whole rows, each a full 128-byte line: 32-deep
+//     steps (64-byte half lines) measured 4% slower at the bench shape.
+//   m/n-contiguous operand [64][COLS]: one row per k, chunk c of row k at c ^ swz_mn(k);
 //     read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one
 //     column, the MFMA operand layout, without a transpose anywhere else.
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 constexpr int kRsrcFlags = 0x00020000;      // raw (unswizzled) 32-bit data, gfx9 family
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used here
-constexpr int kBK = 32;                     // k per pipeline step
-constexpr int kStages = 4;                  // LDS ring depth
+constexpr int kBK = 64;                     // k per pipeline step
+constexpr int kStages = 2;                  // LDS ring depth
 constexpr int kBlockE = 4, kBlockN = 8;     // FWD/DGRAD tile order block
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcFlags);
+  // the range is uniform; readfirstlane keeps it (and the descriptor) in scalar
+  // registers even where it was computed with 64-bit vector compares
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), kRsrcFlags);
 }
 
 __device__ inline uint32_t clamp_bytes(int64_t b) {
@@ -164,8 +169,8 @@ __device__ inline uint32_t clamp_bytes(int64_t b) {
 
 // One 16-byte-per-lane DMA into LDS at byte address lds (uniform). Issued as
 // inline assembly so that the compiler's wait-count pass does not wait for all
-// outstanding DMAs at every LDS read; the k-loop waits for exactly the step it
-// consumes (wait_dma).
+// outstanding DMAs at every LDS read; the k-loop waits for exactly the steps it
+// needs (wait_vm).
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
@@ -182,7 +187,7 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ inline int swz_k(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ inline int swz_k(int r) { return (r >> 1) & 7; }
 __device__ inline int swz_mn(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 10 : 0); }
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -192,11 +197,12 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_char*)p));
 }
 
-// k-contiguous operand tile: ROWS rows x 32 k.
+// k-contiguous operand tile: ROWS rows x 64 k.
 template <int ROWS, int NWAVES>
 struct OpK {
-  static constexpr int BYTES = ROWS * 64;
-  static constexpr int INSTR = BYTES / 1024;  // 16 rows per wavefront DMA
+  static constexpr int ROWB = kBK * 2;
+  static constexpr int BYTES = ROWS * ROWB;
+  static constexpr int INSTR = BYTES / 1024;  // 8 rows per wavefront DMA
   static constexpr int PER_WAVE = INSTR / NWAVES;
   static_assert(INSTR % NWAVES == 0, "DMA split");
   // rsrc base at (row 0, k0); ld in bytes; rows past the range read 0
@@ -205,8 +211,8 @@ struct OpK {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int b = wave + i * NWAVES;
-      const int row = b * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz_k(row);
+      const int row = b * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz_k(row);
       dma16(rs, uint32_t(row) * ld + c * 16, lds + b * 1024);
     }
   }
@@ -214,7 +220,7 @@ struct OpK {
   __device__ static inline bf16x8_t frag(const char* st, int rbase, int ks, int lane) {
     const int row = rbase + (lane & 31);
     const int c = ks * 2 + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(st + row * 64 + ((c ^ swz_k(row)) << 4));
+    return *reinterpret_cast<const bf16x8_t*>(st + row * ROWB + ((c ^ swz_k(row)) << 4));
   }
 };
 
@@ -386,58 +392,67 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 
     // every wavefront has finished reading the ring (previous tile) before refilling it
     __syncthreads();
-#pragma unroll
-    for (int p = 0; p < kStages; ++p)
-      if (p < kiters) issue(p);
+    issue(0);
+    if (kiters > 1) issue(1);
 
+    // Fragments of half a step (two 16-deep substeps) live in registers: a whole
+    // step's would need 96 registers beside the 128 accumulators and spills. Step kt:
+    //   first half   MFMAs of substeps 0, 1; their registers refilled with
+    //                substeps 2, 3 of the same step (the last reads of its stage)
+    //   barrier      step kt+1 is visible to every wavefront, and every read of
+    //                stage kt % 2 has completed, so step kt+2 is issued into it
+    //   second half  MFMAs of substeps 2, 3; registers refilled with substeps 0, 1
+    //                of step kt+1
+    // One LDS read sits between consecutive MFMAs, so the reads run under the
+    // MFMAs and the MFMA pipe never drains at the barrier.
     constexpr int KS = kBK / 16;
-    bf16x8_t fa[KS][FM], fb[KS][FN];
-    // fragments of 16-deep substep ks of step kt
-    auto load = [&](int kt, int ks) {
+    constexpr int HALF = KS / 2;
+    bf16x8_t fa[HALF][FM], fb[HALF][FN];
+    auto load = [&](int kt, int ks, int buf) {
       const char* st = smem + (kt % kStages) * STAGE;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[ks][i] = OA::frag(st, wm * WM + i * 32, ks, lane);
+      for (int i = 0; i < FM; ++i) fa[buf][i] = OA::frag(st, wm * WM + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[ks][j] = OB::frag(st + OA::BYTES, wn * WN + j * 32, ks, lane);
+      for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 32, ks, lane);
     };
-    // wait until at most `later` newer steps' DMAs of this wavefront are in flight
-    auto wait_dma = [&](int later) {
-      if (later >= 3) wait_vm<3 * DMA_PER_STEP>();
-      else if (later == 2) wait_vm<2 * DMA_PER_STEP>();
-      else if (later == 1) wait_vm<DMA_PER_STEP>();
-      else wait_vm<0>();
+    auto mfmas = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     };
-    // before the first barrier, steps 0 .. min(kiters, kStages) - 1 are issued
-    wait_dma(min(kiters - 1, kStages - 1));
+    auto interleave = [&]() {
+#pragma unroll
+      for (int q = 0; q < FM * FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+    };
+    // step 0 landed (step 1 may still be in flight)
+    if (kiters > 1) wait_vm<DMA_PER_STEP>();
+    else wait_vm<0>();
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load(0, ks);
-    // step kt: the fragments of step kt are in registers; before its barrier, steps
-    // up to min(kiters - 1, kt + kStages - 1) are issued. The MFMAs of substep ks
-    // are issued, then its registers are refilled from step kt+1, so LDS reads run
-    // under the MFMAs and the MFMA pipe is not drained at the barrier.
+    for (int h = 0; h < HALF; ++h) load(0, h, h);
     for (int kt = 0; kt < kiters; ++kt) {
       const bool more = kt + 1 < kiters;
-      if (more) wait_dma(min(kiters - kt - 2, kStages - 2));
-      // step kt+1 is visible to every wavefront; every wavefront's reads of step kt
-      // have completed, so stage kt % kStages can be refilled
+#pragma unroll
+      for (int h = 0; h < HALF; ++h) {
+        mfmas(h);
+        load(kt, HALF + h, h);
+        interleave();
+      }
+      if (more) wait_vm<0>();   // this wavefront's DMAs of step kt+1
       __syncthreads();
-      if (kt + kStages < kiters) issue(kt + kStages);
+      if (kt + 2 < kiters) issue(kt + 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
-        // refill (after the last step: re-read this step, in bounds and unused), one
-        // LDS read between consecutive MFMAs
-        load(more ? kt + 1 : kt, ks);
-#pragma unroll
-        for (int q = 0; q < FM * FN; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
+      for (int h = 0; h < HALF; ++h) {
+        mfmas(h);
+        // after the last step: re-read this step's stage (in bounds, no DMA into it
+        // any more, values unused)
+        load(more ? kt + 1 : kt, h, h);
+        interleave();
       }
     }
 
