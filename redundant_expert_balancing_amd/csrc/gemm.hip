@@ -14,22 +14,24 @@
 //   tails   (FWD, DGRAD) the same kernel with 128 x 512 tiles over the tail list:
 //           half the MFMAs a 256 x 256 tile spends on a tail of 1..128 rows.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation; operands go
+// bf16 path: v_mfma_f32_16x16x32_bf16 with float32 accumulation (a 128 x 64
+// wavefront tile as 8 x 4 blocks: per flop, half the accumulator register traffic
+// of the 32 x 32 x 16 form); operands go
 // global -> LDS by DMA into a ring of k-steps; operands stored with M or N
 // contiguous (the weight in FWD, both operands in WGRAD) stay untransposed in
 // LDS and are read with the gfx950 transposing LDS read. A k-step is 64 deep, so
 // every DMA of a k-contiguous operand moves whole 128-byte lines. Each wavefront
 // holds the fragments of half a step in registers and refills them right behind
-// its MFMAs (one LDS read between consecutive MFMAs); the one barrier per step
+// its MFMAs (LDS reads spread between the MFMAs); the one barrier per step
 // sits after the last reads of the step's stage, so a two-stage ring keeps the
 // DMAs one step ahead and the MFMA pipe never drains at the barrier.
 // fp32 path: a plain FMA kernel per output element (tiny layers only).
 //
 // The gate/up projection of the expert FFN can run with its SwiGLU fused into the
-// epilogue: with gate and up columns interleaved in 32-column blocks, the two
-// 32-column MFMA blocks of one wavefront hold the gate and the up value of the
-// same 32 intermediate columns, so each lane forms silu(gate) * up from its own
-// accumulators and the float32 pre-activation never reaches memory.
+// epilogue: with gate and up columns interleaved in 32-column blocks, each 64-column
+// group of a wavefront holds the gate and the up value of the same 32 intermediate
+// columns, so each lane forms silu(gate) * up from its own accumulators and the
+// float32 pre-activation never reaches memory.
 #include <type_traits>
 
 #include "common.h"
@@ -37,7 +39,7 @@
 namespace moonep {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
 
 struct TileEntry {
   int32_t rowbase;  // global buffer row of the segment's first slot: q*SK + cu[q][i]
@@ -202,6 +204,7 @@ template <int ROWS, int NWAVES>
 struct OpK {
   static constexpr int ROWB = kBK * 2;
   static constexpr int BYTES = ROWS * ROWB;
+  static constexpr int READS = 1;               // LDS reads per MFMA operand
   static constexpr int INSTR = BYTES / 1024;  // 8 rows per wavefront DMA
   static constexpr int PER_WAVE = INSTR / NWAVES;
   static_assert(INSTR % NWAVES == 0, "DMA split");
@@ -216,19 +219,20 @@ struct OpK {
       dma16(rs, uint32_t(row) * ld + c * 16, lds + b * 1024);
     }
   }
-  // MFMA operand: rows rbase + lane%32, k = 16*ks + 8*(lane/32) .. +8
+  // MFMA operand: row rbase + lane%16, k = 32*ks + 8*(lane/16) .. +8
   __device__ static inline bf16x8_t frag(const char* st, int rbase, int ks, int lane) {
-    const int row = rbase + (lane & 31);
-    const int c = ks * 2 + (lane >> 5);
+    const int row = rbase + (lane & 15);
+    const int c = ks * 4 + (lane >> 4);
     return *reinterpret_cast<const bf16x8_t*>(st + row * ROWB + ((c ^ swz_k(row)) << 4));
   }
 };
 
-// m/n-contiguous operand tile: 32 k-rows x COLS.
+// m/n-contiguous operand tile: 64 k-rows x COLS.
 template <int COLS, int NWAVES>
 struct OpMN {
   static constexpr int ROWB = COLS * 2;
   static constexpr int CPR = ROWB / 16;         // chunks per row
+  static constexpr int READS = 2;               // LDS reads per MFMA operand
   static constexpr int BYTES = kBK * ROWB;
   static constexpr int INSTR = BYTES / 1024;
   static constexpr int RPI = 1024 / ROWB;       // k rows per wavefront DMA
@@ -247,13 +251,14 @@ struct OpMN {
       dma16(rs, off, lds + b * 1024);
     }
   }
-  // MFMA operand: column cbase + lane%32, k = 16*ks + 8*(lane/32) .. +8, as two
-  // transposed 4x16 reads per 16-lane group
+  // MFMA operand: column cbase + lane%16, k = 32*ks + 8*(lane/16) .. +8, as two
+  // transposed 4x16 reads per 16-lane group: lane i of the group addresses k-row i/4
+  // and columns 4*(i%4) .. +4 and receives the 4 k of column i
   __device__ static inline bf16x8_t frag(const char* st, int cbase, int ks, int lane) {
     const int g = lane >> 4, i = lane & 15;
-    const int col = cbase + 16 * (g & 1) + 4 * (i & 3);
+    const int col = cbase + 4 * (i & 3);
     const int c = col >> 3, half = (col >> 2) & 1;
-    const int k0 = ks * 16 + (g >> 1) * 8 + (i >> 2);
+    const int k0 = ks * 32 + g * 8 + (i >> 2);
     v4s_t v[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -288,10 +293,10 @@ template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int FM = WM / 16, FN = WN / 16;   // 16 x 16 MFMA blocks per wavefront
   static_assert(FM >= 1 && FN >= 1, "tile shape");
-  static_assert(!SWIGLU || (OP == MOONEP_FWD && FN % 2 == 0 && kSwigluBlock == 32),
-                "SwiGLU epilogue: a wavefront holds whole (gate, up) block pairs");
+  static_assert(!SWIGLU || (OP == MOONEP_FWD && FN % 4 == 0 && kSwigluBlock == 32),
+                "SwiGLU epilogue: a wavefront holds whole (gate, up) 32-column block pairs");
   // A stored k-contiguous except in WGRAD; B stored n-contiguous except in DGRAD
   using OA = typename std::conditional<OP == MOONEP_WGRAD, OpMN<BM, NW>, OpK<BM, NW>>::type;
   using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, NW>, OpMN<BN, NW>>::type;
@@ -382,51 +387,55 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       }
     };
 
-    floatx16_t acc[FM][FN];
+    floatx4_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
     // every wavefront has finished reading the ring (previous tile) before refilling it
     __syncthreads();
     issue(0);
     if (kiters > 1) issue(1);
 
-    // Fragments of half a step (two 16-deep substeps) live in registers: a whole
-    // step's would need 96 registers beside the 128 accumulators and spills. Step kt:
-    //   first half   MFMAs of substeps 0, 1; their registers refilled with
-    //                substeps 2, 3 of the same step (the last reads of its stage)
+    // The fragments of half a step (one 32-deep substep: FM + FN operands of 4
+    // registers) live in registers: a whole step's would need 96 registers beside
+    // the 128 accumulators and spills. Step kt:
+    //   first half   MFMAs of substep 0; its registers refilled with substep 1 of
+    //                the same step (the last reads of its stage)
     //   barrier      step kt+1 is visible to every wavefront, and every read of
     //                stage kt % 2 has completed, so step kt+2 is issued into it
-    //   second half  MFMAs of substeps 2, 3; registers refilled with substeps 0, 1
-    //                of step kt+1
-    // One LDS read sits between consecutive MFMAs, so the reads run under the
-    // MFMAs and the MFMA pipe never drains at the barrier.
-    constexpr int KS = kBK / 16;
+    //   second half  MFMAs of substep 1; registers refilled with substep 0 of
+    //                step kt+1
+    // LDS reads are spread between the MFMAs, so they run under the MFMAs and the
+    // MFMA pipe never drains at the barrier.
+    constexpr int KS = kBK / 32;
     constexpr int HALF = KS / 2;
     bf16x8_t fa[HALF][FM], fb[HALF][FN];
     auto load = [&](int kt, int ks, int buf) {
       const char* st = smem + (kt % kStages) * STAGE;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[buf][i] = OA::frag(st, wm * WM + i * 32, ks, lane);
+      for (int i = 0; i < FM; ++i) fa[buf][i] = OA::frag(st, wm * WM + i * 16, ks, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 32, ks, lane);
+      for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 16, ks, lane);
     };
     auto mfmas = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     };
+    // LDS reads per substep: one per k-contiguous fragment, two per transposed one
+    constexpr int READS = FM * OA::READS + FN * OB::READS;
+    constexpr int PER_READ = (FM * FN) / READS > 0 ? (FM * FN) / READS : 1;
     auto interleave = [&]() {
 #pragma unroll
-      for (int q = 0; q < FM * FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      for (int q = 0; q < READS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER_READ, 0);   // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one LDS read
       }
     };
     // step 0 landed (step 1 may still be in flight)
@@ -456,50 +465,54 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       }
     }
 
-    // epilogue: lane holds column (lane % 32) and rows 8*(r/4) + 4*(lane/32) + r%4
-    // of each 32 x 32 block; rows past rows_valid fall outside the range.
-    const int r32 = lane & 31;
+    // epilogue: lane holds column lane % 16 and rows 4 * (lane / 16) + r (r = 0..3)
+    // of each 16 x 16 block; rows past rows_valid fall outside the range.
+    const int r16 = lane & 15;
+    const uint32_t lane_rows = uint32_t(wm * WM + (lane >> 4) * 4);
     if constexpr (SWIGLU) {
-      // block pair (2jp, 2jp+1) of the wavefront = (gate, up) of intermediate columns
+      // in each 64-column group jp of the wavefront, blocks 4jp, 4jp+1 hold the gate
+      // and blocks 4jp+2, 4jp+3 the up value of intermediate columns
       // n0/2 + wn*WN/2 + jp*32 + (0..31); a partial tile ends on a 64-column boundary,
-      // so each pair is all in or all out
+      // so each group is all in or all out
       const int hact = g.Hp / 2;
       const int64_t row0 = int64_t(te.rowbase) + m0;
       const __amdgpu_buffer_rsrc_t ars =
           make_rsrc(g.act + row0 * hact + n0 / 2, clamp_bytes(int64_t(rows_valid) * hact * 2));
-      const uint32_t arow = uint32_t(wm * WM + (lane >> 5) * 4) * hact * 2;
-      uint32_t la[FN / 2];
+      const uint32_t arow = lane_rows * hact * 2;
+      uint32_t la[FN / 4];
 #pragma unroll
-      for (int jp = 0; jp < FN / 2; ++jp)
+      for (int jp = 0; jp < FN / 4; ++jp)
         la[jp] = wn * WN + jp * 64 < cols_valid
-                     ? arow + uint32_t(wn * (WN / 2) + jp * kSwigluBlock + r32) * 2
+                     ? arow + uint32_t(wn * (WN / 2) + jp * kSwigluBlock + r16) * 2
                      : kOffNone;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * hact * 2;
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t rowoff = uint32_t(i * 16 + r) * hact * 2;
 #pragma unroll
-          for (int jp = 0; jp < FN / 2; ++jp) {
-            const float v = swiglu_f32(acc[i][2 * jp][r], acc[i][2 * jp + 1][r]);
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
-                                                  la[jp] + rowoff, 0, 0);
-          }
+          for (int jp = 0; jp < FN / 4; ++jp)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float v = swiglu_f32(acc[i][4 * jp + h][r], acc[i][4 * jp + 2 + h][r]);
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
+                                                    la[jp] + rowoff + h * 32, 0, 0);
+            }
         }
       if (g.h_saved) {
         const __amdgpu_buffer_rsrc_t hrs = make_rsrc(
             g.h_saved + row0 * g.Hp + n0, clamp_bytes(int64_t(rows_valid) * g.Hp * 2));
-        const uint32_t hrow = uint32_t(wm * WM + (lane >> 5) * 4) * g.Hp * 2;
+        const uint32_t hrow = lane_rows * g.Hp * 2;
         uint32_t lh[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          lh[j] = wn * WN + (j / 2) * 64 < cols_valid ? hrow + uint32_t(wn * WN + j * 32 + r32) * 2
+          lh[j] = wn * WN + (j / 4) * 64 < cols_valid ? hrow + uint32_t(wn * WN + j * 16 + r16) * 2
                                                       : kOffNone;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * g.Hp * 2;
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t rowoff = uint32_t(i * 16 + r) * g.Hp * 2;
 #pragma unroll
             for (int j = 0; j < FN; ++j)
               __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][r]),
@@ -521,17 +534,17 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     }
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
     uint32_t lb[FN];
-    const uint32_t lane_row = uint32_t(wm * WM + (lane >> 5) * 4) * ldc * 4;
+    const uint32_t lane_row = lane_rows * ldc * 4;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = wn * WN + j * 32 + r32;
+      const int col = wn * WN + j * 16 + r16;
       lb[j] = col < cols_valid ? lane_row + uint32_t(col) * 4 : kOffNone;
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t rowoff = uint32_t(i * 32 + (r >> 2) * 8 + (r & 3)) * ldc * 4;
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t rowoff = uint32_t(i * 16 + r) * ldc * 4;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const uint32_t off = lb[j] + rowoff;
