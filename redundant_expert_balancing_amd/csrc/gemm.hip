@@ -294,6 +294,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 16, FN = WN / 16;   // 16 x 16 MFMA blocks per wavefront
+  // WGRAD multiplies with the operands swapped, so each accumulator block is the
+  // transpose and a lane holds 4 consecutive columns of one row: its += epilogue
+  // moves 16 bytes per load and store (a quarter of the instructions; 5% faster at
+  // H = 4096, H' = 1408). FWD and DGRAD keep the direct form, which measured faster
+  // for their plain stores.
+  constexpr bool SWAP = OP == MOONEP_WGRAD;
   static_assert(FM >= 1 && FN >= 1, "tile shape");
   static_assert(!SWIGLU || (OP == MOONEP_FWD && FN % 4 == 0 && kSwigluBlock == 32),
                 "SwiGLU epilogue: a wavefront holds whole (gate, up) 32-column block pairs");
@@ -426,7 +432,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+          if constexpr (SWAP)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     };
     // LDS reads per substep: one per k-contiguous fragment, two per transposed one
     constexpr int READS = FM * OA::READS + FN * OB::READS;
@@ -533,6 +542,30 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       ldc = Ndim;
     }
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
+    if constexpr (SWAP) {
+      // lane holds row wm*WM + i*16 + lane%16, columns wn*WN + j*16 + 4*(lane/16) + (0..3);
+      // a 4-column group is all in or all out (the column count is a multiple of 64)
+      const uint32_t lrow = uint32_t(wm * WM + r16) * ldc * 4;
+      uint32_t lc[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * WN + j * 16 + 4 * (lane >> 4);
+        lc[j] = col < cols_valid ? lrow + uint32_t(col) * 4 : kOffNone;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t rowoff = uint32_t(i * 16) * ldc * 4;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t off = lc[j] + rowoff;
+          const floatx4_t old =
+              __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, off, 0, 0));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, old + acc[i][j]), crs,
+                                                 off, 0, 0);
+        }
+      }
+      continue;
+    }
     uint32_t lb[FN];
     const uint32_t lane_row = lane_rows * ldc * 4;
 #pragma unroll
@@ -548,9 +581,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const uint32_t off = lb[j] + rowoff;
-          float v = acc[i][j][r];
-          if (OP == MOONEP_WGRAD)
-            v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(crs, off, 0, 0));
+          // through a scalar: a bit cast applied to the vector element itself reads
+          // element 0 (clang, gfx950 build)
+          const float v = acc[i][j][r];
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), crs, off, 0, 0);
         }
       }
