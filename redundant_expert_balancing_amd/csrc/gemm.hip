@@ -677,15 +677,16 @@ static int device_cus() {
 }
 
 // bf16 tile configuration: 256 x 256 output tiles, 8 wavefronts (two per SIMD, so
-// one wavefront's waits overlap the other's MFMAs) of 128 x 64, 32-deep k-steps in
-// a 4-stage LDS ring (128 KiB), one workgroup per CU. Four wavefronts of 128 x 128
-// (a third fewer LDS bytes per flop) measured 5% slower: one wavefront per SIMD
-// leaves every barrier exposed.
+// one wavefront's waits overlap the other's MFMAs) of 128 x 64, 64-deep k-steps in
+// a 2-stage LDS ring (128 KiB), one workgroup per CU. Four wavefronts of 128 x 128
+// (a third fewer LDS bytes per flop, and a higher clock) measured 11% slower: with
+// one wavefront per SIMD the matrix pipe idles at every wait.
 struct TileCfg {
   static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4;
 };
 // Segment tails of at most kTailRows rows (FWD, DGRAD): 128 x 512 tiles, the same
-// 128 x 64 wavefront tile with the 8 wavefronts side by side in N, a 160 KiB ring.
+// 128 x 64 wavefront tile with the 8 wavefronts side by side in N, a 160 KiB
+// 2-stage ring (16 KiB + 64 KiB per stage).
 // A 256 x 256 tile spends as many MFMAs on a tail of 1..128 rows as on a full one;
 // a 128 x 512 tile covers twice the columns for the same MFMAs.
 struct TailCfg {
