@@ -190,7 +190,12 @@ __device__ inline void wait_vm() {
 }
 
 __device__ inline int swz_k(int r) { return (r >> 1) & 7; }
-__device__ inline int swz_mn(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 10 : 0); }
+// the 4 k-rows one 16-lane group reads take disjoint 32-byte column slots of a
+// 256-byte bank window (k & 3), and the group 8 rows further on, which shares the
+// half-wavefront's pass, takes the 8 slots left free (k & 8)
+__device__ inline int swz_mn(int k) {
+  return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 10 : 0) ^ ((k & 8) ? 2 : 0);
+}
 
 typedef __attribute__((address_space(3))) char lds_char;
 
