@@ -92,9 +92,14 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(cfg, routing, x_dev, w_dev, n_tok: int = 24):
+def cpu_baseline(cfg, routing, x_dev, w_dev, n_tok: int | None = None):
     """The oracle as it stands, on the host: the full plan of one routing plus the
-    dense expert projection and gated combine of ``n_tok`` sampled tokens."""
+    dense expert projection and gated combine of ``n_tok`` sampled tokens (default 2S,
+    two ranks' worth: about 12 s of CPU work at the bench shape; the sample touches
+    every expert, so the per-expert weight conversion is amortised as it would be over
+    the whole batch). The sampled experts' weights are fetched to host memory before
+    the timing."""
+    n_tok = min(cfg.N, 2 * cfg.S if n_tok is None else n_tok)
     import numpy as np
     from oracle import moe as M
     from oracle import plan as P
