@@ -463,22 +463,36 @@ __global__ __launch_bounds__(256) void plan_assign_kernel(
   int32_t* s_ptr = lds + kWavesPerBlock * E;
   int32_t* s_tlo = s_ptr + E + 1;
   int32_t* s_base = s_tlo + max_pieces;
-  const bool valid = flags[kFlagPlanValid] != 0;
-  if (valid) {
-    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_ptr[i] = piece_ptr[i];
-    const int np = min(piece_ptr[E], max_pieces);
-    for (int i = threadIdx.x; i < np; i += blockDim.x) {
-      s_tlo[i] = piece_tlo[i];
-      s_base[i] = piece_base[i];
-    }
-  }
-  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * kWavesPerBlock + w;
-  if (c >= nchunk) return;  // whole wavefront leaves; no block barrier follows
+  const bool have = c < nchunk;
   const int64_t NK = int64_t(N) * K;
   const int64_t u0 = int64_t(c) * kChunkTokens * K;
-  const int64_t u1 = min(NK, u0 + int64_t(kChunkTokens) * K);
+  const int64_t u1 = have ? min(NK, u0 + int64_t(kChunkTokens) * K) : u0;
+  const int nsteps = int((u1 - u0 + 63) / 64);
+  int32_t* run = lds + w * E;  // next rank of every expert inside this chunk
+  // Every global load here is independent of the others, so all are issued before
+  // the one barrier: the ids of the first batch, this chunk's expert bases, and the
+  // whole piece table up to its workspace bound (entries past the plan's count are
+  // never read).
+  int vv[kAssignBatch];
+#pragma unroll
+  for (int j = 0; j < kAssignBatch; ++j) {
+    const int64_t u = u0 + int64_t(j) * 64 + lane;
+    vv[j] = u < u1 ? topk[u] : 0;
+  }
+  if (have) {
+    const int32_t* pp = part + int64_t(c / kScanPart) * E;
+    for (int e = lane; e < E; e += 64) run[e] = base[int64_t(c) * E + e] + pp[e];
+  }
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) s_ptr[i] = piece_ptr[i];
+  for (int i = threadIdx.x; i < max_pieces; i += blockDim.x) {
+    s_tlo[i] = piece_tlo[i];
+    s_base[i] = piece_base[i];
+  }
+  const bool valid = flags[kFlagPlanValid] != 0;
+  __syncthreads();
+  if (!have) return;  // whole wavefront leaves; no block barrier follows
   if (!valid) {
     for (int64_t u = u0 + lane; u < u1; u += 64) {
       slot_map[u] = -1;
@@ -486,21 +500,15 @@ __global__ __launch_bounds__(256) void plan_assign_kernel(
     }
     return;
   }
-  int32_t* run = lds + w * E;  // next rank of every expert inside this chunk
-  const int32_t* pp = part + int64_t(c / kScanPart) * E;
-  for (int e = lane; e < E; e += 64) run[e] = base[int64_t(c) * E + e] + pp[e];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  const int nsteps = int((u1 - u0 + 63) / 64);
   for (int s0 = 0; s0 < nsteps; s0 += kAssignBatch) {
-    int vv[kAssignBatch];
+    if (s0 > 0) {
 #pragma unroll
-    for (int j = 0; j < kAssignBatch; ++j) {
-      const int64_t u = u0 + int64_t(s0 + j) * 64 + lane;
-      vv[j] = u < u1 ? topk[u] : 0;
+      for (int j = 0; j < kAssignBatch; ++j) {
+        const int64_t u = u0 + int64_t(s0 + j) * 64 + lane;
+        vv[j] = u < u1 ? topk[u] : 0;
+      }
     }
 #pragma unroll
     for (int j = 0; j < kAssignBatch; ++j) {
