@@ -47,7 +47,7 @@ def check_plan(topk_idx, R, S, E, K, B, mode, cu_seqlens, replica_expert,
         if (np.diff(cu[q]) < 0).any():
             bad.append(f"I1 rank {q} cu_seqlens decreasing")
     # I2
-    if sm.min() < 0 or sm.max() >= n or len(set(sm.tolist())) != n:
+    if n and (sm.min() < 0 or sm.max() >= n or len(set(sm.tolist())) != n):
         bad.append("I2 slot_map not a bijection")
         return bad
     for u in range(n):

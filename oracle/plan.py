@@ -44,7 +44,7 @@ def expert_loads(topk_idx: np.ndarray, E: int) -> np.ndarray:
 
     [maestro "The problem MoonEP targets"] names T_e the tokens routed to e.
     """
-    return np.bincount(np.asarray(topk_idx).reshape(-1), minlength=E).astype(np.int64)
+    return np.bincount(np.asarray(topk_idx, dtype=np.int64).reshape(-1), minlength=E)
 
 
 def maxvio(T: np.ndarray, R: int, S: int, K: int, E: int) -> float:
