@@ -104,11 +104,15 @@ def test_plan_balanced_and_star():
 
 
 def test_plan_empty_layer():
-    cfg = small_cfg(R=4, S=0, E=16, K=2)
-    layer = PlanOnly(cfg)
-    got, _ = plan_on_gpu(layer, np.zeros((0, 2), dtype=np.int32))
-    assert (got["cu_seqlens"] == 0).all()
-    assert (got["replica_expert"] == -1).all()
+    """S = 0 in both modes: the plan equals the oracle's (all rows empty, no slots)."""
+    for mode, B in (("train", None), ("infer", 2)):
+        cfg = small_cfg(R=4, S=0, E=16, K=2, B=B, mode=mode)
+        layer = PlanOnly(cfg)
+        topk = np.zeros((0, 2), dtype=np.int32)
+        got, _ = plan_on_gpu(layer, topk)
+        assert_plan_equal(got, P.plan(topk, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode))
+        assert (got["cu_seqlens"] == 0).all()
+        assert (got["replica_expert"] == -1).all()
 
 
 def test_plan_invalid_ids_flagged_and_plan_emptied():
