@@ -18,8 +18,8 @@ violated properties (empty = valid).
   I6  training: B = E/R and no overflow rows, so every touched expert is local;
       inference: overflow rows only once all B slots are used
   I7  within a row segment, slots keep ascending flat slot id (the stated order
-      of the zero-copy buffer; a choice of this build, checked separately by
-      ``check_order``)
+      of the zero-copy buffer; the pages fix no order, so this is a chosen
+      reading, checked separately by ``check_order``)
 """
 from __future__ import annotations
 
