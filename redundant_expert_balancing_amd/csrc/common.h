@@ -77,7 +77,7 @@ __device__ inline float swiglu_f32(float g, float u) { return g / (1.0f + expf(-
 // + p % kSwigluBlock and its up projection kSwigluBlock further.
 constexpr int kSwigluBlock = MOONEP_SWIGLU_BLOCK;
 
-// Host-side validation shared by all entry points (defined in api.cpp).
+// Host-side validation shared by all entry points (defined in api.hip).
 int validate(const moonep_shape* s);
 int elem_bytes(const moonep_shape& s);
 int launch_status();  // MOONEP_OK or MOONEP_EHIP after the last launch

@@ -7,7 +7,7 @@
 //   tiles   one workgroup turns cu_seqlens [R, E+B+1] into compact lists of work
 //           entries (segment start row, weight row, M offset, length): 256-row
 //           M-tiles, and (FWD, DGRAD) a second list of segment tails of at most
-//           128 rows.
+//           128 rows; WGRAD's entries are whole segments, longest first.
 //   gemm    a persistent kernel walks entry x N-tile (x M-tile for WGRAD) with
 //           256 x 256 tiles; the 32 concurrent tiles of one XCD form a block of 4
 //           entries x 8 N-tiles, so they share operand slices in that XCD's L2.
@@ -59,12 +59,21 @@ __device__ inline int wave_scan_incl(int v) {
   return v;
 }
 
+// Whole-segment entries (WGRAD) are listed longest first when there are at most
+// this many: the length of a WGRAD tile's k-loop is its segment's, which ranges
+// over orders of magnitude under skew, and the persistent grid takes tiles in list
+// order, so long tiles at the end leave most CUs idle.
+constexpr int kSortMax = 4096;
+
 // M-tiles of bm rows per segment (bm = 0: one entry per whole segment). With
 // tail > 0 a segment's last M-tile goes to a second list when it has at most
 // `tail` rows: those are computed by a kernel with tail-row M-tiles and twice
-// the N width, so a short tail costs half as many MFMAs.
+// the N width, so a short tail costs half as many MFMAs. With bm = 0 and
+// longest_first the entries are ordered by segment length, descending (ties in
+// (rank, row) order); every tile owns its outputs, so the order changes no result.
 __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restrict__ cu, int R,
                                                           int E, int B, int SK, int bm, int tail,
+                                                          bool longest_first,
                                                           TileEntry* __restrict__ tiles,
                                                           int32_t* __restrict__ ntiles,
                                                           int max_tiles,
@@ -72,6 +81,7 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ ntails,
                                                           int max_tails) {
   __shared__ int swave[2][17];
+  __shared__ uint64_t skey[kSortMax];
   const int EB = E + B, total = R * EB;
   const int per = (total + 1023) / 1024;
   const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
@@ -110,6 +120,46 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
   __syncthreads();
   int k = swave[0][w] + incl - cnt;
   int kt = swave[1][w] + incl_t - cnt_tail;
+  const int count = swave[0][16];
+  if (threadIdx.x == 0) {
+    *ntiles = min(count, max_tiles);
+    *ntails = min(swave[1][16], max_tails);
+  }
+  if (bm <= 0 && longest_first && count <= kSortMax && count <= max_tiles) {
+    // key: (length descending, segment index ascending); padding sorts last
+    for (int idx = i0; idx < i1; ++idx) {
+      const int q = idx / EB, i = idx % EB;
+      const int n = cu[q * (EB + 1) + i + 1] - cu[q * (EB + 1) + i];
+      if (n <= 0) continue;
+      skey[k++] = (uint64_t(0x7FFFFFFF - n) << 32) | uint32_t(idx);
+    }
+    int P = 1;
+    while (P < count) P <<= 1;
+    for (int j = count + threadIdx.x; j < P; j += 1024) skey[j] = ~uint64_t(0);
+    __syncthreads();
+    // bitonic sort of skey[0, P), ascending
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = threadIdx.x; t < P / 2; t += 1024) {
+          const int lo = 2 * stride * (t / stride) + t % stride, hi = lo + stride;
+          const uint64_t a = skey[lo], b = skey[hi];
+          if ((a > b) == ((lo & size) == 0)) {
+            skey[lo] = b;
+            skey[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int j = threadIdx.x; j < count; j += 1024) {
+      const int idx = int(uint32_t(skey[j]));
+      const int q = idx / EB, i = idx % EB;
+      const int c0 = cu[q * (EB + 1) + i];
+      const int n = cu[q * (EB + 1) + i + 1] - c0;
+      tiles[j] = TileEntry{q * SK + c0, i < E ? i : E + q * B + (i - E), 0, n};
+    }
+    return;
+  }
   for (int idx = i0; idx < i1; ++idx) {
     const int q = idx / EB, i = idx % EB;
     const int c0 = cu[q * (EB + 1) + i];
@@ -127,10 +177,6 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
       if (kt < max_tails) tails[kt] = TileEntry{q * SK + c0, wrow, f * step, n};
       ++kt;
     }
-  }
-  if (threadIdx.x == 0) {
-    *ntiles = min(swave[0][16], max_tiles);
-    *ntails = min(swave[1][16], max_tails);
   }
 }
 
@@ -157,6 +203,7 @@ constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used h
 constexpr int kBK = 64;                     // k per pipeline step
 constexpr int kStages = 2;                  // LDS ring depth
 constexpr int kBlockE = 4, kBlockN = 8;     // FWD/DGRAD tile order block
+constexpr int kEpiAhead = 4;                // WGRAD epilogue: row blocks read ahead of the stores
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // the range is uniform; readfirstlane keeps it (and the descriptor) in scalar
@@ -557,17 +604,28 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
         const int col = wn * WN + j * 16 + 4 * (lane >> 4);
         lc[j] = col < cols_valid ? lrow + uint32_t(col) * 4 : kOffNone;
       }
+      // The += reads run kEpiAhead row blocks ahead of the stores. The compiler keeps
+      // buffer loads and stores in program order (it cannot tell that they never
+      // overlap), so a read written after the previous block's stores would wait for a
+      // whole memory round trip of its own: FM * FN of them in a row per tile.
+      constexpr int AHEAD = kEpiAhead < FM ? kEpiAhead : FM;
+      floatx4_t old[FM][FN];
+      auto read_old = [&](int i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          old[i][j] = __builtin_bit_cast(
+              floatx4_t,
+              __builtin_amdgcn_raw_buffer_load_b128(crs, lc[j] + uint32_t(i * 16) * ldc * 4, 0, 0));
+      };
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) read_old(i);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint32_t rowoff = uint32_t(i * 16) * ldc * 4;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const uint32_t off = lc[j] + rowoff;
-          const floatx4_t old =
-              __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, off, 0, 0));
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, old + acc[i][j]), crs,
-                                                 off, 0, 0);
-        }
+        for (int j = 0; j < FN; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, old[i][j] + acc[i][j]),
+                                                 crs, lc[j] + uint32_t(i * 16) * ldc * 4, 0, 0);
+        if (i + AHEAD < FM) read_old(i + AHEAD);
       }
       continue;
     }
@@ -764,8 +822,8 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
   const bool tails_apart = mtiled && split_tails(s, op == MOONEP_DGRAD ? s.H : s.Hp, cus);
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
                                           mtiled ? TileCfg::BM : 0, tails_apart ? kTailRows : 0,
-                                          tiles, ntiles, int(w.max_tiles), tails, ntails,
-                                          int(w.max_tail));
+                                          bf16 && op == MOONEP_WGRAD, tiles, ntiles,
+                                          int(w.max_tiles), tails, ntails, int(w.max_tail));
   if (launch_status()) return MOONEP_EHIP;
 
   if (bf16) {
@@ -811,8 +869,8 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
   if (cus <= 0) return MOONEP_EHIP;
   const bool tails_apart = bf16 && split_tails(s, 2 * s.Hp, cus);
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
-                                          bf16 ? TileCfg::BM : 0, tails_apart ? kTailRows : 0, tiles,
-                                          ntiles, int(w.max_tiles), tails, ntails,
+                                          bf16 ? TileCfg::BM : 0, tails_apart ? kTailRows : 0,
+                                          false, tiles, ntiles, int(w.max_tiles), tails, ntails,
                                           int(w.max_tail));
   if (launch_status()) return MOONEP_EHIP;
   if (bf16) {
