@@ -32,6 +32,7 @@
 // group of a wavefront holds the gate and the up value of the same 32 intermediate
 // columns, so each lane forms silu(gate) * up from its own accumulators and the
 // float32 pre-activation never reaches memory.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -763,17 +764,21 @@ __global__ __launch_bounds__(256) void gemm_fp32_swiglu_kernel(
 }
 
 // ------------------------------------------------------------------ host
+// Compute units of the current device, cached per device. Host threads may call
+// concurrently: every store of an entry writes the same value.
 static int device_cus() {
-  static int cached_dev = -1, cached = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev != cached_dev) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached_dev = dev;
-    cached = n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cached;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // bf16 tile configuration: 256 x 256 output tiles, 8 wavefronts (two per SIMD, so
