@@ -63,7 +63,9 @@ __device__ inline int wave_scan_incl(int v) {
 // Whole-segment entries (WGRAD) are listed longest first when there are at most
 // this many: the length of a WGRAD tile's k-loop is its segment's, which ranges
 // over orders of magnitude under skew, and the persistent grid takes tiles in list
-// order, so long tiles at the end leave most CUs idle.
+// order, so long tiles at the end leave most CUs idle. A training plan has at most
+// E + R*B = 2E <= 2048 non-empty segments, so every planned WGRAD is sorted; larger
+// counts (cu_seqlens from elsewhere, up to R*(E+B) <= 8192 rows) keep plan order.
 constexpr int kSortMax = 4096;
 
 // M-tiles of bm rows per segment (bm = 0: one entry per whole segment). With
