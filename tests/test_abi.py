@@ -57,6 +57,14 @@ def S(**kw):
     (dict(dtype=3), L.EINVAL),
     (dict(R=1, E=2048, B=2048, K=8), L.ELIMIT),           # E > 1024
     (dict(R=64, E=256, B=4), L.ELIMIT),                   # R*(E+B+1) > 8192
+    (dict(R=8, E=928, B=95, mode=L.INFER), L.OK),         # R*(E+B+1) = 8192 exactly
+    (dict(R=8, E=928, B=96, mode=L.INFER), L.ELIMIT),     # 8200
+    (dict(R=4, E=64, B=16, K=32), L.OK),                  # K = 32, the largest
+    (dict(R=4, E=64, B=16, K=33), L.EINVAL),
+    (dict(R=1, E=1024, B=1024, K=8), L.OK),               # E = 1024, the largest
+    (dict(R=1, E=1025, B=1025, K=8), L.ELIMIT),           # E > 1024
+    (dict(R=8, E=1024, B=0, K=8, mode=L.INFER), L.ELIMIT),  # E = 1024, 8 ranks: 8200
+    (dict(R=4, E=1024, B=0, K=8, mode=L.INFER), L.OK),    # E = 1024: 4100
 ])
 def test_validate_shape(kw, status):
     assert L.moonep_validate_shape(S(**kw)) == status

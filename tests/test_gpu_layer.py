@@ -290,7 +290,9 @@ def test_per_rank_subproblems_reproduce_the_full_gemm():
     dict(R=2, S=24, E=64, K=32, H=64, Hp=128),                 # K = 32
     dict(R=1, S=77, E=16, K=4, B=0, H=128, Hp=64, mode="infer"),   # one rank, no slots
     dict(R=8, S=33, E=32, K=2, B=1, H=192, Hp=320, mode="infer"),  # overflow into home rows
-], ids=["E1024", "K1_ragged_tiles", "K32", "R1_B0", "infer_B1"])
+    dict(R=8, S=30, E=928, K=8, B=95, H=64, Hp=64, mode="infer"),  # R*(E+B+1) = 8192, the limit
+    dict(R=64, S=8, E=64, K=2, H=64, Hp=128),                  # 64 ranks of one expert, B = 1
+], ids=["E1024", "K1_ragged_tiles", "K32", "R1_B0", "infer_B1", "rows_limit", "R64"])
 def test_edge_shapes_full_compare(kw):
     """Forward (and backward where the layer trains) compared element by element with
     the oracle at edge shapes of the plan and of the GEMM tiling."""

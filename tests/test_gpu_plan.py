@@ -70,6 +70,8 @@ EDGE = [
     (16, 33, 256, 8, "infer", 4, list(range(16))),      # inference overflow
     (5, 129, 25, 4, "infer", 2, [0, 1, 2, 3, 4]),       # odd sizes everywhere
     (32, 8, 128, 4, "train", None, [0]),         # many ranks
+    (64, 16, 64, 2, "train", None, [0, 1]),      # 64 ranks of one expert each (B = 1)
+    (8, 100, 928, 8, "infer", 95, list(range(40))),  # R*(E+B+1) = 8192, the size limit
 ]
 
 
