@@ -101,9 +101,44 @@ def strerror(status: int) -> str:
     return lib().moonep_strerror(status).decode()
 
 
-def _p(t):
-    """Device pointer of a tensor (None -> NULL)."""
-    return None if t is None else _vp(t.data_ptr())
+def _p(t, nbytes: int = 0, name: str = "buffer", dtype=None):
+    """Device pointer of a tensor (None -> NULL). The tensor must be a contiguous GPU
+    tensor of at least `nbytes` bytes (and of `dtype`, if given): anything else raises
+    here, before a kernel could read or write past it."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: a GPU tensor is required, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: the tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, the call needs at least {nbytes}")
+    return _vp(t.data_ptr())
+
+
+def _dims(shape: Shape):
+    """(elements per token row N, slots N*K, slots per rank SK, bytes per element)."""
+    N = shape.R * shape.S
+    return N, N * shape.K, shape.S * shape.K, 2 if shape.dtype == BF16 else 4
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _act(shape: Shape):
+    """torch dtype of the layer's activations and weights."""
+    import torch
+    return torch.bfloat16 if shape.dtype == BF16 else torch.float32
 
 
 def _s(stream):
@@ -136,56 +171,106 @@ def moonep_workspace_bytes(shape: Shape) -> int:
 
 
 def moonep_workspace_init(shape, ws, stream=None):
-    _check("moonep_workspace_init",
-           lib().moonep_workspace_init(ctypes.byref(shape), _p(ws), _nbytes(ws), _s(stream)))
+    _check("moonep_workspace_init", lib().moonep_workspace_init(
+        ctypes.byref(shape), _p(ws, moonep_workspace_bytes(shape), "ws"), _nbytes(ws), _s(stream)))
 
 
 def moonep_plan(shape, topk_idx, cu_seqlens, replica_expert, slot_map, src_index, ws, stream=None):
+    N, NK, _, _ = _dims(shape)
+    i32, R, B = _i32(), shape.R, shape.B
     _check("moonep_plan", lib().moonep_plan(
-        ctypes.byref(shape), _p(topk_idx), _p(cu_seqlens), _p(replica_expert), _p(slot_map),
-        _p(src_index), _p(ws), _nbytes(ws), _s(stream)))
+        ctypes.byref(shape), _p(topk_idx, 4 * NK, "topk_idx", i32),
+        _p(cu_seqlens, 4 * R * (shape.E + B + 1), "cu_seqlens", i32),
+        _p(replica_expert, 4 * R * B, "replica_expert", i32),
+        _p(slot_map, 4 * NK, "slot_map", i32), _p(src_index, 4 * NK, "src_index", i32),
+        _p(ws, moonep_workspace_bytes(shape), "ws"), _nbytes(ws), _s(stream)))
+
+
+def _w_all_bytes(shape: Shape) -> int:
+    return (shape.E + shape.R * shape.B) * shape.H * shape.Hp * _dims(shape)[3]
 
 
 def moonep_prefetch_weight(shape, replica_expert, w_all, stream=None):
     _check("moonep_prefetch_weight", lib().moonep_prefetch_weight(
-        ctypes.byref(shape), _p(replica_expert), _p(w_all), _s(stream)))
+        ctypes.byref(shape), _p(replica_expert, 4 * shape.R * shape.B, "replica_expert", _i32()),
+        _p(w_all, _w_all_bytes(shape), "w_all", _act(shape)), _s(stream)))
 
 
 def moonep_dispatch(shape, width, src, slot_map, gates, dst, stream=None):
+    N, NK, _, eb = _dims(shape)
+    w = int(width)
     _check("moonep_dispatch", lib().moonep_dispatch(
-        ctypes.byref(shape), int(width), _p(src), _p(slot_map), _p(gates), _p(dst), _s(stream)))
+        ctypes.byref(shape), w, _p(src, N * w * eb, "src", _act(shape)),
+        _p(slot_map, 4 * NK, "slot_map", _i32()), _p(gates, 4 * NK, "gates", _f32()),
+        _p(dst, NK * w * eb, "dst", _act(shape)), _s(stream)))
 
 
 def moonep_grouped_gemm(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, ws, stream=None):
+    _, NK, _, eb = _dims(shape)
+    H, Hp, act = shape.H, shape.Hp, _act(shape)
+    wsz = 4 * H * Hp
+    if int(op) == FWD:
+        args = (_p(a, NK * H * eb, "a (xp)", act), _p(b, _w_all_bytes(shape), "b (w_all)", act),
+                _p(c, 4 * NK * Hp, "c (out)", _f32()), None, None)
+    elif int(op) == DGRAD:
+        args = (_p(a, NK * Hp * eb, "a (dyp)", act), _p(b, _w_all_bytes(shape), "b (w_all)", act),
+                _p(c, 4 * NK * H, "c (dxp)", _f32()), None, None)
+    elif int(op) == WGRAD:
+        args = (_p(a, NK * H * eb, "a (xp)", act), _p(b, NK * Hp * eb, "b (dyp)", act), None,
+                _p(grad_home, shape.E * wsz, "grad_home", _f32()),
+                _p(reduce_buf, shape.R * shape.B * wsz, "reduce_buf", _f32()))
+    else:
+        args = (_p(a), _p(b), _p(c), _p(grad_home), _p(reduce_buf))   # the library refuses op
     _check("moonep_grouped_gemm", lib().moonep_grouped_gemm(
-        ctypes.byref(shape), int(op), _p(a), _p(b), _p(cu_seqlens), _p(c), _p(grad_home),
-        _p(reduce_buf), _p(ws), _nbytes(ws), _s(stream)))
+        ctypes.byref(shape), int(op), args[0], args[1],
+        _p(cu_seqlens, 4 * shape.R * (shape.E + shape.B + 1), "cu_seqlens", _i32()),
+        args[2], args[3], args[4], _p(ws, moonep_workspace_bytes(shape), "ws"), _nbytes(ws),
+        _s(stream)))
 
 
 def moonep_combine(shape, width, src, slot_map, gates, dst, stream=None):
+    N, NK, _, _ = _dims(shape)
+    w = int(width)
     _check("moonep_combine", lib().moonep_combine(
-        ctypes.byref(shape), int(width), _p(src), _p(slot_map), _p(gates), _p(dst), _s(stream)))
+        ctypes.byref(shape), w, _p(src, 4 * NK * w, "src", _f32()),
+        _p(slot_map, 4 * NK, "slot_map", _i32()), _p(gates, 4 * NK, "gates", _f32()),
+        _p(dst, 4 * N * w, "dst", _f32()), _s(stream)))
 
 
 def moonep_reduce_grad(shape, replica_expert, reduce_buf, grad_home, stream=None):
+    wsz = 4 * shape.H * shape.Hp
     _check("moonep_reduce_grad", lib().moonep_reduce_grad(
-        ctypes.byref(shape), _p(replica_expert), _p(reduce_buf), _p(grad_home), _s(stream)))
+        ctypes.byref(shape), _p(replica_expert, 4 * shape.R * shape.B, "replica_expert", _i32()),
+        _p(reduce_buf, shape.R * shape.B * wsz, "reduce_buf", _f32()),
+        _p(grad_home, shape.E * wsz, "grad_home", _f32()), _s(stream)))
 
 
 def moonep_swiglu(shape, h, act, h_saved=None, stream=None):
-    _check("moonep_swiglu", lib().moonep_swiglu(ctypes.byref(shape), _p(h), _p(act), _p(h_saved),
-                                                _s(stream)))
+    _, NK, _, eb = _dims(shape)
+    Hp = shape.Hp
+    _check("moonep_swiglu", lib().moonep_swiglu(
+        ctypes.byref(shape), _p(h, 4 * NK * 2 * Hp, "h", _f32()),
+        _p(act, NK * Hp * eb, "act", _act(shape)),
+        _p(h_saved, NK * 2 * Hp * eb, "h_saved", _act(shape)), _s(stream)))
 
 
 def moonep_grouped_gemm_swiglu(shape, xp, w1_all, cu_seqlens, act, h_saved, ws, stream=None):
+    _, NK, _, eb = _dims(shape)
+    H, Hp, a = shape.H, shape.Hp, _act(shape)
     _check("moonep_grouped_gemm_swiglu", lib().moonep_grouped_gemm_swiglu(
-        ctypes.byref(shape), _p(xp), _p(w1_all), _p(cu_seqlens), _p(act), _p(h_saved), _p(ws),
-        _nbytes(ws), _s(stream)))
+        ctypes.byref(shape), _p(xp, NK * H * eb, "xp", a),
+        _p(w1_all, (shape.E + shape.R * shape.B) * H * 2 * Hp * eb, "w1_all", a),
+        _p(cu_seqlens, 4 * shape.R * (shape.E + shape.B + 1), "cu_seqlens", _i32()),
+        _p(act, NK * Hp * eb, "act", a), _p(h_saved, NK * 2 * Hp * eb, "h_saved", a),
+        _p(ws, moonep_workspace_bytes(shape), "ws"), _nbytes(ws), _s(stream)))
 
 
 def moonep_swiglu_backward(shape, h_saved, da, dh, stream=None):
+    _, NK, _, eb = _dims(shape)
+    Hp, a = shape.Hp, _act(shape)
     _check("moonep_swiglu_backward", lib().moonep_swiglu_backward(
-        ctypes.byref(shape), _p(h_saved), _p(da), _p(dh), _s(stream)))
+        ctypes.byref(shape), _p(h_saved, NK * 2 * Hp * eb, "h_saved", a),
+        _p(da, 4 * NK * Hp, "da", _f32()), _p(dh, NK * 2 * Hp * eb, "dh", a), _s(stream)))
 
 
 def moonep_vm_granularity() -> int:
@@ -223,5 +308,6 @@ def moonep_view_destroy(view):
 def moonep_get_error(shape, ws, clear: bool = False) -> int:
     flags = ctypes.c_int32(0)
     _check("moonep_get_error", lib().moonep_get_error(
-        ctypes.byref(shape), _p(ws), _nbytes(ws), ctypes.byref(flags), int(clear)))
+        ctypes.byref(shape), _p(ws, moonep_workspace_bytes(shape), "ws"), _nbytes(ws),
+        ctypes.byref(flags), int(clear)))
     return flags.value

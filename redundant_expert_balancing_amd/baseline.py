@@ -73,7 +73,10 @@ def home_only_ranks(cfg, xp_sorted, cu_sorted, w_home):
     for q in range(cfg.R):
         start, rows = bounds[q], bounds[q + 1] - bounds[q]
         cu = (cu_sorted[q * G:(q + 1) * G + 1] - start).to(torch.int32).view(1, G + 1)
-        shape = _one_rank_shape(G, max(1, -(-rows // K)), K, 0, cfg.H, cfg.Hp, "infer", cfg.dtype)
-        a = xp_sorted[start:start + max(rows, 1)]
+        S = max(1, -(-rows // K))
+        shape = _one_rank_shape(G, S, K, 0, cfg.H, cfg.Hp, "infer", cfg.dtype)
+        # the rank's rows, padded with zero rows to the S*K rows its shape declares
+        a = torch.zeros((S * K, cfg.H), dtype=xp_sorted.dtype, device=xp_sorted.device)
+        a[:rows] = xp_sorted[start:start + rows]
         probs.append(RankProblem(shape, a, w_home[q * G:(q + 1) * G].contiguous(), cu))
     return probs, [b - a for a, b in zip(bounds[:-1], bounds[1:])]

@@ -132,3 +132,17 @@ def test_pool_calls_validate_before_any_hip_call():
     assert lib.moonep_pool_destroy(None) == L.EINVAL
     assert lib.moonep_view_destroy(None) == L.EINVAL
     assert lib.moonep_pool_bytes(None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    """The Python binding hands the library device pointers only: a host tensor is
+    refused before any call (it would otherwise reach a kernel as an address)."""
+    import torch
+    sh = S()
+    N, NK = sh.R * sh.S, sh.R * sh.S * sh.K
+    x = torch.zeros((N, sh.H), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.moonep_dispatch(sh, sh.H, x, x, None, x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.moonep_combine(sh, sh.Hp, torch.zeros(NK * sh.Hp), torch.zeros(NK, dtype=torch.int32),
+                         None, torch.zeros(N * sh.Hp))

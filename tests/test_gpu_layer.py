@@ -15,6 +15,7 @@ import torch
 
 from oracle import moe as M
 from oracle import plan as P
+from redundant_expert_balancing_amd import _lib as L
 from redundant_expert_balancing_amd.layer import MoEProjection
 from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
 
@@ -377,3 +378,30 @@ def test_random_layers_full_compare(i):
         assert not np.any(gh[idle])
         assert rel_err(gh[active], dW_ref[active]) <= tolerance(cfg)
         assert int(torch.count_nonzero(layer.reduce_buf)) == 0
+
+
+def test_binding_refuses_wrong_buffers():
+    """Buffers too small, of the wrong dtype or not contiguous are refused by the
+    binding before any launch; the layer still works afterwards."""
+    cfg = CONFIGS["bf16_train_mild"]
+    say("binding checks")
+    r, layer, d, topk, gates = _setup(cfg, cfg.maxvio[0])
+    sh = layer.shape
+    x = d["x"]
+    with pytest.raises(ValueError, match="bytes"):
+        L.moonep_dispatch(sh, cfg.H, x, layer.slot_map, None, layer.xp[: layer.xp.shape[0] // 2])
+    with pytest.raises(ValueError, match="dtype"):
+        L.moonep_dispatch(sh, cfg.H, x.float(), layer.slot_map, None, layer.xp)
+    with pytest.raises(ValueError, match="contiguous"):
+        L.moonep_combine(sh, cfg.Hp, layer.out.t(), layer.slot_map, gates, layer.y)
+    with pytest.raises(ValueError, match="bytes"):
+        L.moonep_grouped_gemm(sh, L.FWD, layer.xp, layer.w_all[: cfg.E], layer.cu_seqlens,
+                              layer.out, None, None, layer.ws)
+    with pytest.raises(ValueError, match="bytes"):
+        L.moonep_plan(sh, topk, layer.cu_seqlens, layer.replica_expert, layer.slot_map,
+                      layer.src_index, layer.ws[:16])
+    y = layer.forward(topk, x, gates)
+    torch.cuda.synchronize()
+    assert layer.error_flags() == 0
+    x_h, W_h = _host(x), _host(d["W"][:cfg.E])
+    assert rel_err(_host(y), M.dense_forward(x_h, W_h, r.topk_idx, r.gates)) <= tolerance(cfg)
