@@ -818,12 +818,13 @@ static void launch_cfg(const GemmArgs& g, int cus, hipStream_t strm) {
       <<<cus, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
-// the full-tile list, then (FWD and DGRAD) the tail list on the tail kernel
+// the full-tile list, then (FWD and DGRAD, when the tails are split off) the tail list
+// on the tail kernel
 template <int OP, bool SWIGLU = false>
-static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntails, int cus,
-                        hipStream_t strm) {
+static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntails,
+                        bool tails_apart, int cus, hipStream_t strm) {
   launch_cfg<OP, SWIGLU, TileCfg>(g, cus, strm);
-  if constexpr (OP != MOONEP_WGRAD) {
+  if (OP != MOONEP_WGRAD && tails_apart) {
     g.tiles = tails;
     g.ntiles = ntails;
     launch_cfg<OP, SWIGLU, TailCfg>(g, cus, strm);
@@ -873,9 +874,9 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
   if (bf16) {
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
                reduce_buf, tiles, ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
-    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, tails, ntails, cus, strm);
-    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, tails, ntails, cus, strm);
-    else launch_bf16<MOONEP_WGRAD>(g, tails, ntails, cus, strm);
+    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, tails, ntails, tails_apart, cus, strm);
+    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, tails, ntails, tails_apart, cus, strm);
+    else launch_bf16<MOONEP_WGRAD>(g, tails, ntails, false, cus, strm);
   } else {
     const dim3 grid(64, 256);
     const float* af = static_cast<const float*>(a);
@@ -921,7 +922,7 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
     GemmArgs g{static_cast<const uint16_t*>(xp), static_cast<const uint16_t*>(w1_all), nullptr,
                nullptr, nullptr, tiles, ntiles, s.H, 2 * s.Hp, s.E,
                static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved)};
-    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, cus, strm);
+    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, tails_apart, cus, strm);
   } else {
     gemm_fp32_swiglu_kernel<<<dim3(64, 256), 256, 0, strm>>>(
         static_cast<const float*>(xp), static_cast<const float*>(w1_all),
