@@ -16,6 +16,9 @@ replicas and overflow occur), and checks:
   DeepEP v2");
 * in training, the backward pipeline (gated dY, segment dgrad and wgrad, unpermute,
   reduce_grad) against the dense gradients, with the consumed slots left at zero.
+
+The draws are derandomized (a fixed seed per test), so every run checks the same
+examples; ten times as many draws also passed when these tests were written.
 """
 import numpy as np
 from hypothesis import HealthCheck, given, settings
@@ -51,7 +54,8 @@ def _routing(R, S, E, K, seed, hot):
     return topk, gates, rng
 
 
-@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=300, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
 @given(layers())
 def test_plan_invariants_and_order(layer):
     R, S, E, K, B, mode, seed, hot = layer
@@ -64,7 +68,8 @@ def test_plan_invariants_and_order(layer):
     assert pl.n_replicas <= R * B
 
 
-@settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=120, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
 @given(layers(), st.integers(1, 9), st.integers(1, 9))
 def test_pipeline_equals_dense_definition(layer, H, Hp):
     R, S, E, K, B, mode, seed, hot = layer
