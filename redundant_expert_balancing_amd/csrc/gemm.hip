@@ -207,6 +207,14 @@ constexpr int kBK = 64;                     // k per pipeline step
 constexpr int kStages = 2;                  // LDS ring depth
 constexpr int kBlockE = 4, kBlockN = 8;     // FWD/DGRAD tile order block
 constexpr int kEpiAhead = 4;                // WGRAD epilogue: row blocks read ahead of the stores
+// Cache policy of streaming output stores (nt sc1), and the longest reduction for which
+// DGRAD stores its float32 output that way. With 22 k-steps per tile (H' = 1408) the
+// output leaves fast enough to push operand lines out of L2: streaming stores made that
+// DGRAD 4.3% faster (2970-3003 -> 2848-2868 us, three A/B pairs on one box), while they
+// were neutral or slightly slower for every longer reduction and for FWD (the FFN down
+// projection 1% slower).
+constexpr int kStreamStore = 18;
+constexpr int kStreamOutMaxK = 1536;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // the range is uniform; readfirstlane keeps it (and the descriptor) in scalar
@@ -344,7 +352,8 @@ struct GemmArgs {
   uint16_t* h_saved;  // SwiGLU epilogue: NULL or bf16 [rows, Hp]
 };
 
-template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false>
+template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false,
+          bool STREAM_OUT = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -687,7 +696,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
           // through a scalar: a bit cast applied to the vector element itself reads
           // element 0 (clang, gfx950 build)
           const float v = acc[i][j][r];
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), crs, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), crs, off, 0,
+                                                STREAM_OUT ? kStreamStore : 0);
         }
       }
   }
@@ -812,22 +822,22 @@ static bool split_tails(const moonep_shape& s, int ncols, int cus) {
   return full >= 4 * int64_t(cus);
 }
 
-template <int OP, bool SWIGLU, typename C>
+template <int OP, bool SWIGLU, typename C, bool STREAM_OUT = false>
 static void launch_cfg(const GemmArgs& g, int cus, hipStream_t strm) {
-  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU>
+  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU, STREAM_OUT>
       <<<cus, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
 // the full-tile list, then (FWD and DGRAD, when the tails are split off) the tail list
 // on the tail kernel
-template <int OP, bool SWIGLU = false>
+template <int OP, bool SWIGLU = false, bool STREAM_OUT = false>
 static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntails,
                         bool tails_apart, int cus, hipStream_t strm) {
-  launch_cfg<OP, SWIGLU, TileCfg>(g, cus, strm);
+  launch_cfg<OP, SWIGLU, TileCfg, STREAM_OUT>(g, cus, strm);
   if (OP != MOONEP_WGRAD && tails_apart) {
     g.tiles = tails;
     g.ntiles = ntails;
-    launch_cfg<OP, SWIGLU, TailCfg>(g, cus, strm);
+    launch_cfg<OP, SWIGLU, TailCfg, STREAM_OUT>(g, cus, strm);
   }
 }
 
@@ -875,6 +885,8 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
                reduce_buf, tiles, ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
     if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, tails, ntails, tails_apart, cus, strm);
+    else if (op == MOONEP_DGRAD && s.Hp <= kStreamOutMaxK)
+      launch_bf16<MOONEP_DGRAD, false, true>(g, tails, ntails, tails_apart, cus, strm);
     else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, tails, ntails, tails_apart, cus, strm);
     else launch_bf16<MOONEP_WGRAD>(g, tails, ntails, false, cus, strm);
   } else {
