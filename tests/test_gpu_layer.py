@@ -255,7 +255,12 @@ def test_per_rank_subproblems_reproduce_the_full_gemm():
     """The per-rank views used by the no-redundancy baseline: each balanced rank's
     one-rank GEMM equals its rows of the full grouped GEMM; each home-only rank's
     GEMM equals its rows of the one-rank (counting-sort) plan's GEMM; and that plan
-    computes every (token, k) slot to the same bits as the balanced plan."""
+    computes every (token, k) slot to the same bits as the balanced plan. Against
+    the oracle: the plain-EP rank loads are oracle.plan.home_only_loads, and every
+    row of every per-rank problem, balanced and plain EP, is x[g] @ W[e] of the slot
+    the oracle's plan puts there [ai-maestro.online "Moonshot AI open-sources
+    MoonEP", section "The problem MoonEP targets": with plain EP the hottest rank
+    holds all of its experts' tokens]."""
     from redundant_expert_balancing_amd.baseline import balanced_rank, home_only_ranks
     from redundant_expert_balancing_amd.synth import LayerConfig
     cfg = CONFIGS["bf16_train_mild"]
@@ -267,21 +272,32 @@ def test_per_rank_subproblems_reproduce_the_full_gemm():
     layer1.forward(topk, d["x"], gates)
     torch.cuda.synchronize()
     SK = cfg.S * cfg.K
+    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
+    pl1 = P.plan(r.topk_idx, 1, cfg.N, cfg.E, cfg.K, 0, "infer")
+    assert np.array_equal(layer.src_index.cpu().numpy(), pl.src_index)
+    assert np.array_equal(layer1.src_index.cpu().numpy(), pl1.src_index)
+    # every slot's oracle value, indexed by flat slot id u = g*K + k
+    out_ref = M.dense_expert_outputs(_host(d["x"]), _host(d["W"][:cfg.E]), r.topk_idx)
     for q in range(cfg.R):
         p = balanced_rank(layer, q)
         p.run()
         torch.cuda.synchronize()
         assert torch.equal(p.out, layer.out[q * SK:(q + 1) * SK]), q
+        e = rel_err(_host(p.out), out_ref[pl.src_index[q * SK:(q + 1) * SK]])
+        assert e <= tolerance(cfg), ("balanced rank", q, e)
     probs, rows = home_only_ranks(cfg, layer1.xp, layer1.cu_seqlens[0], d["W"])
+    assert rows == P.home_only_loads(r.topk_idx, cfg.R, cfg.E)
     assert sum(rows) == cfg.N * cfg.K
     start = 0
     for q, p in enumerate(probs):
         p.run()
         torch.cuda.synchronize()
         assert torch.equal(p.out[:rows[q]], layer1.out[start:start + rows[q]]), q
+        e = rel_err(_host(p.out[:rows[q]]), out_ref[pl1.src_index[start:start + rows[q]]])
+        say("plain-EP rank", q, "rows", rows[q], "max err / RMS", e)
+        assert e <= tolerance(cfg), ("plain-EP rank", q, e)
         start += rows[q]
     assert torch.equal(layer1.out[layer1.slot_map.long()], layer.out[layer.slot_map.long()])
-    pl = P.plan(r.topk_idx, cfg.R, cfg.S, cfg.E, cfg.K, cfg.B, cfg.mode)
     assert rows == pl.L
 
 

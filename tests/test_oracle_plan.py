@@ -240,3 +240,40 @@ def test_order_checker_rejects_unstable_segment():
     si = np.argsort(sm).astype(np.int32)
     assert check_plan(topk, 2, 2, 4, 1, 2, "train", pl.cu_seqlens, pl.replica_expert, sm, si) == []
     assert check_order(pl.cu_seqlens, si, 2, 2, 1, 4, 2) != []
+
+
+# ----------------------------------------------------------------- plain-EP loads
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: c["name"])
+def test_home_only_loads_hand_worked(case):
+    """Rows each rank computes with no redundant experts (plain EP: every slot goes
+    to its expert's home rank), against the loads worked by hand in each case."""
+    c = case
+    topk = np.array(c["topk_idx"], dtype=np.int32)
+    assert P.home_only_loads(topk, c["R"], c["E"]) == c["L"]
+
+
+def test_home_only_loads_brute_force():
+    """Against a literal count: visit every (token, k) slot and credit the rank that
+    owns its expert (e // (E/R)); the loads add up to every slot, and the balanced
+    plan starts from the same loads and ends with exactly S*K on every rank."""
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        R = int(rng.integers(1, 7))
+        G = int(rng.integers(1, 5))
+        E = R * G
+        K = int(rng.integers(1, min(E, 4) + 1))
+        S = int(rng.integers(0, 9))
+        p = rng.dirichlet(np.full(E, 0.3))
+        topk = np.array([rng.choice(E, K, replace=False, p=p) for _ in range(R * S)],
+                        dtype=np.int32).reshape(R * S, K)
+        want = [0] * R
+        for g in range(R * S):
+            for k in range(K):
+                want[int(topk[g, k]) // G] += 1
+        got = P.home_only_loads(topk, R, E)
+        assert got == want
+        assert sum(got) == R * S * K
+        pl = P.plan(topk, R, S, E, K, G, "train")
+        assert list(pl.L) == want
+        assert all(int(pl.cu_seqlens[q, -1]) == S * K for q in range(R))
