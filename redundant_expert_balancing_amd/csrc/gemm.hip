@@ -25,7 +25,8 @@
 // its MFMAs (LDS reads spread between the MFMAs); the one barrier per step
 // sits after the last reads of the step's stage, so a two-stage ring keeps the
 // DMAs one step ahead and the MFMA pipe never drains at the barrier.
-// fp32 path: a plain FMA kernel per output element (tiny layers only).
+// fp32 path: one thread per output element, each dot product accumulated with error
+// compensation (as if in twice the working precision; tiny layers only).
 //
 // The gate/up projection of the expert FFN can run with its SwiGLU fused into the
 // epilogue: with gate and up columns interleaved in 32-column blocks, each 64-column
@@ -704,6 +705,32 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 }
 
 // ------------------------------------------------------------------ fp32 kernel
+// Compensated dot product (Ogita, Rump and Oishi, "Accurate sum and dot product",
+// SIAM J. Sci. Comput. 26(6), 2005, algorithm Dot2): every product is split into its
+// rounded value and its exact error by one FMA, every addition into its rounded sum
+// and its exact error by Knuth's branch-free two-sum, and the errors are summed on
+// the side. The result is as accurate as a dot product evaluated in twice the float32
+// precision and then rounded: |err| <= u*|dot| + O(n^2 u^2) * sum|a_i b_i|, with no
+// sqrt(n) growth over long reductions. Contraction stays off so that every rounded
+// product and sum is the one the error terms describe.
+struct Dot2 {
+  float p = 0.f, s = 0.f;
+  __device__ inline void add(float a, float b) {
+#pragma clang fp contract(off)
+    const float h = a * b;
+    const float r = fmaf(a, b, -h);      // a*b - h exactly
+    const float x = p + h;
+    const float z = x - p;
+    const float q = (p - (x - z)) + (h - z);   // p + h - x exactly
+    p = x;
+    s = s + (q + r);
+  }
+  __device__ inline float value() const {
+#pragma clang fp contract(off)
+    return p + s;
+  }
+};
+
 // One thread per output element; FWD/DGRAD over tile entries of whole segments.
 template <int OP>
 __global__ __launch_bounds__(256) void gemm_fp32_kernel(const float* __restrict__ a,
@@ -724,27 +751,27 @@ __global__ __launch_bounds__(256) void gemm_fp32_kernel(const float* __restrict_
         const int m = int(idx / Ndim), n = int(idx % Ndim);
         const float* ar = a + (int64_t(te.rowbase) + m) * Kdim;
         const float* w = b + int64_t(te.wrow) * wsz;
-        float s = 0.f;
+        Dot2 d;
         for (int k = 0; k < Kdim; ++k)
-          s = fmaf(ar[k], OP == MOONEP_FWD ? w[int64_t(k) * Hp + n] : w[int64_t(n) * Hp + k], s);
-        c[(int64_t(te.rowbase) + m) * Ndim + n] = s;
+          d.add(ar[k], OP == MOONEP_FWD ? w[int64_t(k) * Hp + n] : w[int64_t(n) * Hp + k]);
+        c[(int64_t(te.rowbase) + m) * Ndim + n] = d.value();
       }
     } else {
       float* dst = te.wrow < E ? grad_home + int64_t(te.wrow) * wsz
                                : reduce_buf + int64_t(te.wrow - E) * wsz;
       for (int64_t idx = blockIdx.x * 256 + threadIdx.x; idx < wsz; idx += int64_t(gridDim.x) * 256) {
         const int h = int(idx / Hp), p = int(idx % Hp);
-        float s = 0.f;
+        Dot2 d;
         for (int t2 = 0; t2 < te.n; ++t2)
-          s = fmaf(a[(int64_t(te.rowbase) + t2) * H + h], b[(int64_t(te.rowbase) + t2) * Hp + p], s);
-        dst[idx] += s;
+          d.add(a[(int64_t(te.rowbase) + t2) * H + h], b[(int64_t(te.rowbase) + t2) * Hp + p]);
+        dst[idx] += d.value();
       }
     }
   }
 }
 
 // fp32 gate/up projection with the SwiGLU fused: one thread per (row, intermediate
-// column) forms the gate and the up sums in the same order as gemm_fp32_kernel.
+// column) forms the gate and the up sums as gemm_fp32_kernel does.
 __global__ __launch_bounds__(256) void gemm_fp32_swiglu_kernel(
     const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ act,
     float* __restrict__ h_saved, const TileEntry* __restrict__ tiles,
@@ -761,11 +788,12 @@ __global__ __launch_bounds__(256) void gemm_fp32_swiglu_kernel(
       const int64_t row = int64_t(te.rowbase) + m;
       const float* ar = a + row * H;
       const float* w = b + int64_t(te.wrow) * wsz;
-      float sg = 0.f, su = 0.f;
+      Dot2 dg, du;
       for (int k = 0; k < H; ++k) {
-        sg = fmaf(ar[k], w[int64_t(k) * H2 + gc], sg);
-        su = fmaf(ar[k], w[int64_t(k) * H2 + gc + kSwigluBlock], su);
+        dg.add(ar[k], w[int64_t(k) * H2 + gc]);
+        du.add(ar[k], w[int64_t(k) * H2 + gc + kSwigluBlock]);
       }
+      const float sg = dg.value(), su = du.value();
       act[row * Hact + p] = swiglu_f32(sg, su);
       if (h_saved) {
         h_saved[row * H2 + gc] = sg;

@@ -7,8 +7,7 @@ the float64 oracle (oracle/ffn.py) on the same inputs.
 Small layers are compared element by element everywhere, full-size layers on
 sampled tokens and experts. The fused and the unfused gate/up paths must agree
 bit for bit (same float32 accumulators, same activation function). Tolerances:
-max abs error <= 1e-2 * RMS(reference) for bf16 layers, <= 1e-5 * RMS for fp32
-(3e-5 for the float32 backward, derived where it is checked);
+max abs error <= 1e-2 * RMS(reference) for bf16 layers, <= 1e-5 * RMS for fp32;
 the standalone SwiGLU kernels within one bfloat16 rounding step (bf16) or a few
 float32 ulps (fp32) of the oracle, element by element.
 """
@@ -232,12 +231,7 @@ def _ffn_backward_check(cfg, target, alpha=None, full=False):
     want = (gates.reshape(-1)[u][:, None] * d["dyH"].float()[u // cfg.K]).to(layer.dtype)
     assert torch.equal(layer.dyp[sm], want)
     N, K = cfg.R * cfg.S, cfg.K
-    # float32 layers: the backward chains two float32 GEMMs through the SwiGLU
-    # gradient; weight-gradient entries are sequential float32 sums over a segment
-    # (up to ~150 slots here), whose random-walk error sqrt(n) * 2^-24 of the
-    # partial sums reaches 1-2e-5 * RMS at the largest of ~10^6 entries. The
-    # forward bar (1e-5 * RMS) stays for the forward checks.
-    tol = tolerance(cfg) if cfg.dtype == "bf16" else 3e-5
+    tol = tolerance(cfg)
     if full:
         x_h, dy_h = _host(d["x"]), _host(d["dyH"])
         W1, W2 = _host(d["W1"][:cfg.E]), _host(d["W2"][:cfg.E])
