@@ -189,5 +189,7 @@ def plan(topk_idx: np.ndarray, R: int, S: int, E: int, K: int, B: int, mode: str
 
 
 def home_only_loads(topk_idx: np.ndarray, R: int, E: int) -> list[int]:
-    """Rows each rank would receive with no redundancy (plain EP): L_p."""
+    """Rows each rank computes with no redundant experts (plain EP): every slot goes to
+    the home rank of its expert, so rank p holds L_p, whatever the skew [maestro "The
+    problem MoonEP targets": the hottest rank sets the layer's time]."""
     return rank_loads(expert_loads(topk_idx, E), R)
