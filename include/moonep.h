@@ -177,6 +177,29 @@ int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const void* a, co
                         const int32_t* cu_seqlens, float* c, float* grad_home, float* reduce_buf,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the per-device scratch array behind moonep_grouped_gemm_noalloc. */
+#define MOONEP_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
+
+/*
+ * moonep_grouped_gemm for callers that cannot allocate device memory or hold a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments (without the workspace), results and errors
+ * as moonep_grouped_gemm, on the same kernels. Its tile lists live in a static
+ * device array of MOONEP_NOALLOC_SCRATCH_BYTES, one per device, held until the
+ * process ends; the call allocates nothing, frees nothing and needs no set-up
+ * (the first call on a device resolves the array's address once).
+ * Limit: the lists of one call take 256 + align256(16 * (R*(ceil(S*K/64) + E + B)
+ * + 1)) + 16 * (R*(E+B) + 1) bytes rounded up to 256 (0.23 MiB at R=8, S=8192,
+ * K=8, E=384, B=48); a shape that needs more than the array returns
+ * MOONEP_ELIMIT before any launch.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's lists: calls that can overlap on one device (two streams, two host
+ * threads) race and must be ordered by the caller.
+ */
+int moonep_grouped_gemm_noalloc(const moonep_shape* shape, int32_t op, const void* a,
+                                const void* b, const int32_t* cu_seqlens, float* c,
+                                float* grad_home, float* reduce_buf, void* stream);
+
 /*
  * Fused unpermute: dst[g] = sum over k ascending of gates[g][k] * src[slot_map[g*K+k]]
  * (gates NULL: weight 1 -- the unpermute of dX), float32 [maestro "The core

@@ -23,7 +23,7 @@ OK, EINVAL, EWORKSPACE, EHIP, EMODE, ELIMIT = 0, -1, -2, -3, -4, -5
 EXPORTS = (
     "moonep_version", "moonep_strerror", "moonep_validate_shape", "moonep_workspace_bytes",
     "moonep_workspace_init", "moonep_plan", "moonep_prefetch_weight", "moonep_dispatch",
-    "moonep_grouped_gemm", "moonep_combine", "moonep_reduce_grad", "moonep_get_error",
+    "moonep_grouped_gemm", "moonep_grouped_gemm_noalloc", "moonep_combine", "moonep_reduce_grad", "moonep_get_error",
     "moonep_swiglu", "moonep_grouped_gemm_swiglu", "moonep_swiglu_backward",
     "moonep_vm_granularity", "moonep_pool_create", "moonep_pool_bytes", "moonep_pool_destroy",
     "moonep_view_create", "moonep_view_destroy",
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
             "moonep_dispatch": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
             "moonep_grouped_gemm": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp], ctypes.c_int),
+            "moonep_grouped_gemm_noalloc": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _vp], ctypes.c_int),
             "moonep_combine": ([_sp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
             "moonep_reduce_grad": ([_sp, _vp, _vp, _vp, _vp], ctypes.c_int),
             "moonep_get_error": ([_sp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32),
@@ -205,7 +207,7 @@ def moonep_dispatch(shape, width, src, slot_map, gates, dst, stream=None):
         _p(dst, NK * w * eb, "dst", _act(shape)), _s(stream)))
 
 
-def moonep_grouped_gemm(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, ws, stream=None):
+def _gemm_operands(shape, op, a, b, c, grad_home, reduce_buf):
     _, NK, _, eb = _dims(shape)
     H, Hp, act = shape.H, shape.Hp, _act(shape)
     wsz = 4 * H * Hp
@@ -221,11 +223,25 @@ def moonep_grouped_gemm(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, w
                 _p(reduce_buf, shape.R * shape.B * wsz, "reduce_buf", _f32()))
     else:
         args = (_p(a), _p(b), _p(c), _p(grad_home), _p(reduce_buf))   # the library refuses op
+    return args
+
+
+def moonep_grouped_gemm(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, ws, stream=None):
+    args = _gemm_operands(shape, op, a, b, c, grad_home, reduce_buf)
     _check("moonep_grouped_gemm", lib().moonep_grouped_gemm(
         ctypes.byref(shape), int(op), args[0], args[1],
         _p(cu_seqlens, 4 * shape.R * (shape.E + shape.B + 1), "cu_seqlens", _i32()),
         args[2], args[3], args[4], _p(ws, moonep_workspace_bytes(shape), "ws"), _nbytes(ws),
         _s(stream)))
+
+
+def moonep_grouped_gemm_noalloc(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf,
+                                stream=None):
+    args = _gemm_operands(shape, op, a, b, c, grad_home, reduce_buf)
+    _check("moonep_grouped_gemm_noalloc", lib().moonep_grouped_gemm_noalloc(
+        ctypes.byref(shape), int(op), args[0], args[1],
+        _p(cu_seqlens, 4 * shape.R * (shape.E + shape.B + 1), "cu_seqlens", _i32()),
+        args[2], args[3], args[4], _s(stream)))
 
 
 def moonep_combine(shape, width, src, slot_map, gates, dst, stream=None):

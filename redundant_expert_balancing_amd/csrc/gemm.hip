@@ -873,31 +873,44 @@ static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntail
 
 using namespace moonep;
 
-extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const void* a,
-                                   const void* b, const int32_t* cu_seqlens, float* c,
-                                   float* grad_home, float* reduce_buf, void* ws, size_t ws_bytes,
-                                   void* stream) {
+namespace moonep {
+
+// Where one grouped-GEMM call keeps its tile lists and their two counts.
+struct GemmLists {
+  TileEntry* tiles;
+  TileEntry* tails;
+  int32_t* ntiles;
+  int32_t* ntails;
+  int64_t max_tiles, max_tail;
+};
+
+// Argument checks shared by the workspace and the scratch entry points; MOONEP_OK
+// with `empty` set when there is nothing to compute.
+static int gemm_args(const moonep_shape* shape, int32_t op, const void* a, const void* b,
+                     const int32_t* cu_seqlens, float* c, float* grad_home, float* reduce_buf,
+                     bool& empty) {
   int st = validate(shape);
   if (st) return st;
   const moonep_shape& s = *shape;
   if (op != MOONEP_FWD && op != MOONEP_DGRAD && op != MOONEP_WGRAD) return MOONEP_EINVAL;
   if (op != MOONEP_FWD && s.mode != MOONEP_TRAIN) return MOONEP_EMODE;
   if (s.H % 64 || s.Hp % 64) return MOONEP_EINVAL;
-  if (!aligned16(cu_seqlens) || !aligned16(ws)) return MOONEP_EINVAL;
-  const WsLayout w = ws_layout(s);
-  if (ws_bytes < w.total) return MOONEP_EWORKSPACE;
-  if (s.S == 0) return MOONEP_OK;
+  if (!aligned16(cu_seqlens)) return MOONEP_EINVAL;
+  empty = s.S == 0;
+  if (empty) return MOONEP_OK;
   if (!aligned16(a) || !aligned16(b)) return MOONEP_EINVAL;
   if (op == MOONEP_WGRAD) {
     if (!aligned16(grad_home) || (s.B > 0 && !aligned16(reduce_buf))) return MOONEP_EINVAL;
   } else if (!aligned16(c)) {
     return MOONEP_EINVAL;
   }
-  hipStream_t strm = as_stream(stream);
-  TileEntry* tiles = ws_ptr<TileEntry>(ws, w.tiles);
-  TileEntry* tails = ws_ptr<TileEntry>(ws, w.tiles_tail);
-  int32_t* ntiles = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount;
-  int32_t* ntails = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail;
+  return MOONEP_OK;
+}
+
+// The tile-list kernel, then the GEMM kernel(s) of `op`, all on `strm`.
+static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const void* b,
+                       const int32_t* cu_seqlens, float* c, float* grad_home, float* reduce_buf,
+                       const GemmLists& w, hipStream_t strm) {
   const bool bf16 = s.dtype == MOONEP_BF16;
   const bool mtiled = bf16 && op != MOONEP_WGRAD;
   const int cus = device_cus();
@@ -905,30 +918,109 @@ extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const 
   const bool tails_apart = mtiled && split_tails(s, op == MOONEP_DGRAD ? s.H : s.Hp, cus);
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
                                           mtiled ? TileCfg::BM : 0, tails_apart ? kTailRows : 0,
-                                          bf16 && op == MOONEP_WGRAD, tiles, ntiles,
-                                          int(w.max_tiles), tails, ntails, int(w.max_tail));
+                                          bf16 && op == MOONEP_WGRAD, w.tiles, w.ntiles,
+                                          int(w.max_tiles), w.tails, w.ntails, int(w.max_tail));
   if (launch_status()) return MOONEP_EHIP;
 
   if (bf16) {
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
-               reduce_buf, tiles, ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
-    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, tails, ntails, tails_apart, cus, strm);
+               reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
+    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, w.tails, w.ntails, tails_apart, cus, strm);
     else if (op == MOONEP_DGRAD && s.Hp <= kStreamOutMaxK)
-      launch_bf16<MOONEP_DGRAD, false, true>(g, tails, ntails, tails_apart, cus, strm);
-    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, tails, ntails, tails_apart, cus, strm);
-    else launch_bf16<MOONEP_WGRAD>(g, tails, ntails, false, cus, strm);
+      launch_bf16<MOONEP_DGRAD, false, true>(g, w.tails, w.ntails, tails_apart, cus, strm);
+    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, w.tails, w.ntails, tails_apart, cus, strm);
+    else launch_bf16<MOONEP_WGRAD>(g, w.tails, w.ntails, false, cus, strm);
   } else {
     const dim3 grid(64, 256);
     const float* af = static_cast<const float*>(a);
     const float* bfp = static_cast<const float*>(b);
     if (op == MOONEP_FWD)
-      gemm_fp32_kernel<MOONEP_FWD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, tiles, ntiles, s.H, s.Hp, s.E);
+      gemm_fp32_kernel<MOONEP_FWD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E);
     else if (op == MOONEP_DGRAD)
-      gemm_fp32_kernel<MOONEP_DGRAD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, tiles, ntiles, s.H, s.Hp, s.E);
+      gemm_fp32_kernel<MOONEP_DGRAD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E);
     else
-      gemm_fp32_kernel<MOONEP_WGRAD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, tiles, ntiles, s.H, s.Hp, s.E);
+      gemm_fp32_kernel<MOONEP_WGRAD><<<grid, 256, 0, strm>>>(af, bfp, c, grad_home, reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E);
   }
   return launch_status();
+}
+
+static GemmLists ws_lists(void* ws, const WsLayout& w) {
+  return GemmLists{ws_ptr<TileEntry>(ws, w.tiles), ws_ptr<TileEntry>(ws, w.tiles_tail),
+                   ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount,
+                   ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail, w.max_tiles, w.max_tail};
+}
+
+// ------------------------------------------------------------------ no-alloc scratch
+// Tile lists of moonep_grouped_gemm_noalloc live in this file-scope device array, one
+// copy per device, held until the process ends. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): its device
+// address is resolved once per device with hipGetSymbolAddress and used from then on.
+static __device__ __align__(256) char scratch[MOONEP_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (nullptr on failure), resolved on
+// the first call with that device current and cached per device. Concurrent first
+// calls resolve the same address.
+static char* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<char*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  char* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  cache[dev].store(static_cast<char*>(q), std::memory_order_release);
+  return static_cast<char*>(q);
+}
+
+// Scratch layout of one call: the two list counts, then the two lists, each 256-byte
+// aligned, sized as the workspace sizes them.
+struct ScratchLayout {
+  size_t tiles, tails, total;
+};
+static ScratchLayout scratch_layout(const WsLayout& w) {
+  ScratchLayout l{};
+  l.tiles = 256;
+  l.tails = align256(l.tiles + size_t(w.max_tiles) * sizeof(TileEntry));
+  l.total = align256(l.tails + size_t(w.max_tail) * sizeof(TileEntry));
+  return l;
+}
+
+}  // namespace moonep
+
+extern "C" int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const void* a,
+                                   const void* b, const int32_t* cu_seqlens, float* c,
+                                   float* grad_home, float* reduce_buf, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  bool empty = false;
+  int st = gemm_args(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, empty);
+  if (st) return st;
+  if (!aligned16(ws)) return MOONEP_EINVAL;
+  const WsLayout w = ws_layout(*shape);
+  if (ws_bytes < w.total) return MOONEP_EWORKSPACE;
+  if (empty) return MOONEP_OK;
+  return gemm_launch(*shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, ws_lists(ws, w),
+                     as_stream(stream));
+}
+
+extern "C" int moonep_grouped_gemm_noalloc(const moonep_shape* shape, int32_t op, const void* a,
+                                           const void* b, const int32_t* cu_seqlens, float* c,
+                                           float* grad_home, float* reduce_buf, void* stream) {
+  bool empty = false;
+  int st = gemm_args(shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, empty);
+  if (st) return st;
+  const WsLayout w = ws_layout(*shape);
+  const ScratchLayout l = scratch_layout(w);
+  if (l.total > MOONEP_NOALLOC_SCRATCH_BYTES) return MOONEP_ELIMIT;
+  if (empty) return MOONEP_OK;
+  char* base = scratch_ptr();
+  if (!base) return MOONEP_EHIP;
+  const GemmLists lists{reinterpret_cast<TileEntry*>(base + l.tiles),
+                        reinterpret_cast<TileEntry*>(base + l.tails),
+                        reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base) + 1,
+                        w.max_tiles, w.max_tail};
+  return gemm_launch(*shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, lists,
+                     as_stream(stream));
 }
 
 extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void* xp,

@@ -42,6 +42,17 @@ int main(void) {
   CHECK(moonep_grouped_gemm(&inf, MOONEP_DGRAD, p, p, p, p, NULL, NULL, p, (size_t)1 << 30,
                             NULL) == MOONEP_EMODE);
   CHECK(moonep_reduce_grad(&inf, p, p, p, NULL) == MOONEP_EMODE);
+  /* the no-alloc GEMM: the same argument checks, and shapes whose tile lists exceed its
+   * scratch array refused before any device call */
+  CHECK(moonep_grouped_gemm_noalloc(&s, 7, p, p, p, p, NULL, NULL, NULL) == MOONEP_EINVAL);
+  CHECK(moonep_grouped_gemm_noalloc(&inf, MOONEP_DGRAD, p, p, p, p, NULL, NULL, NULL) ==
+        MOONEP_EMODE);
+  moonep_shape big = s;
+  big.S = 131072; /* R*ceil(S*K/64) = 131072 list entries: 2 MiB of tiles alone */
+  CHECK(moonep_validate_shape(&big) == MOONEP_OK);
+  CHECK(moonep_grouped_gemm_noalloc(&big, MOONEP_FWD, p, p, p, p, NULL, NULL, NULL) ==
+        MOONEP_ELIMIT);
+  CHECK(MOONEP_NOALLOC_SCRATCH_BYTES == (size_t)2 << 20);
   moonep_pool* pool = NULL;
   CHECK(moonep_pool_create(&bad, 1, &pool) == MOONEP_EINVAL && pool == NULL);
   CHECK(moonep_view_destroy(NULL) == MOONEP_EINVAL);
