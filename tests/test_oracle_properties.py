@@ -12,8 +12,8 @@ replicas and overflow occur), and checks:
 * the stable order of every segment (global token order);
 * the float64 pipeline (prefetch, permute, segment products, gated combine) against
   the plan-free dense definition y[g] = sum_k gate[g,k] x[g] W[topk[g,k]], and so
-  its independence of B ("no impact on correctness", same page, "Benchmarks against
-  DeepEP v2");
+  its independence of B (the B setting does not change the results: same page,
+  "The memory contract");
 * in training, the backward pipeline (gated dY, segment dgrad and wgrad, unpermute,
   reduce_grad) against the dense gradients, with the consumed slots left at zero.
 
