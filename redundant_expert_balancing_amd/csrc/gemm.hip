@@ -205,7 +205,6 @@ typedef short v4s_t __attribute__((ext_vector_type(4)));
 constexpr int kRsrcFlags = 0x00020000;      // raw (unswizzled) 32-bit data, gfx9 family
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used here
 constexpr int kBK = 64;                     // k per pipeline step
-constexpr int kStages = 2;                  // LDS ring depth
 constexpr int kBlockE = 4, kBlockN = 8;     // FWD/DGRAD tile order block
 constexpr int kEpiAhead = 4;                // WGRAD epilogue: row blocks read ahead of the stores
 // Cache policy of streaming output stores (nt sc1), and the longest reduction for which
@@ -354,7 +353,7 @@ struct GemmArgs {
 };
 
 template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false,
-          bool STREAM_OUT = false>
+          bool STREAM_OUT = false, int STAGES = 2>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -373,7 +372,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, NW>, OpMN<BN, NW>>::type;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int DMA_PER_STEP = OA::PER_WAVE + OB::PER_WAVE;
-  __shared__ __align__(1024) char smem[kStages * STAGE];
+  static_assert(STAGES >= 2 && (STAGES & (STAGES - 1)) == 0, "LDS ring depth: a power of two");
+  __shared__ __align__(1024) char smem[STAGES * STAGE];
 
   const int Ndim = OP == MOONEP_DGRAD ? g.H : g.Hp;   // columns of C
   const int Kfix = OP == MOONEP_FWD ? g.H : g.Hp;     // FWD/DGRAD reduction length
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   // runs under the last half step and the += epilogue; the next tile's base is that
   // stage. WGRAD measured 3.5% faster at H = 4096, H' = 1408; FWD within noise and
   // DGRAD (22 k-steps per tile there) 2% slower, so they start every tile afresh.
-  constexpr bool NEXT_STEP0 = OP == MOONEP_WGRAD;
+  constexpr bool NEXT_STEP0 = OP == MOONEP_WGRAD && STAGES == 2;
   int base = 0;
   bool step0_issued = false;
   for (int64_t tau = slot; tau < total; tau += G) {
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     const int cols_valid = cur.cols_valid, kdim = cur.kdim;
     const int kiters = (kdim + kBK - 1) / kBK;
     const bool has_next = NEXT_STEP0 && tau + G < total;
-    auto stage = [&](int kt) { return uint32_t((base + kt) & 1) * STAGE; };
+    auto stage = [&](int kt) { return uint32_t((base + kt) & (STAGES - 1)) * STAGE; };
     auto issue = [&](int kt) { issue_task(cur, kt, lds0 + stage(kt)); };
 
     floatx4_t acc[FM][FN];
@@ -500,7 +500,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     // every wavefront has finished reading the ring (previous tile) before refilling it
     __syncthreads();
     if (!step0_issued) issue(0);
-    if (kiters > 1) issue(1);
+#pragma unroll
+    for (int k = 1; k < STAGES; ++k)
+      if (k < kiters) issue(k);
+    // wait until at most n later steps of this wavefront's DMAs are in flight
+    auto wait_steps = [&](int n) {
+      if constexpr (STAGES > 3) {
+        if (n >= 3) { wait_vm<3 * DMA_PER_STEP>(); return; }
+      }
+      if constexpr (STAGES > 2) {
+        if (n == 2) { wait_vm<2 * DMA_PER_STEP>(); return; }
+      }
+      if (n == 1) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
+    };
 
     // The fragments of half a step (one 32-deep substep: FM + FN operands of 4
     // registers) live in registers: a whole step's would need 96 registers beside
@@ -543,9 +556,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one LDS read
       }
     };
-    // step 0 landed (step 1 may still be in flight)
-    if (kiters > 1) wait_vm<DMA_PER_STEP>();
-    else wait_vm<0>();
+    // step 0 landed (the later steps of the ring may still be in flight)
+    wait_steps(min(STAGES, kiters) - 1);
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < HALF; ++h) load(0, h, h);
@@ -557,9 +569,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
         load(kt, HALF + h, h);
         interleave();
       }
-      if (more) wait_vm<0>();   // this wavefront's DMAs of step kt+1
+      // this wavefront's DMAs of step kt+1 (steps up to kt+STAGES-1 may be in flight)
+      if (more) wait_steps(min(kt + STAGES - 1, kiters - 1) - (kt + 1));
       __syncthreads();
-      if (kt + 2 < kiters) issue(kt + 2);
+      if (kt + STAGES < kiters) issue(kt + STAGES);
       else if (!more && has_next) issue_task(task_at(tau + G), 0, lds0 + stage(kt));
 #pragma unroll
       for (int h = 0; h < HALF; ++h) {
@@ -827,7 +840,7 @@ static int device_cus() {
 // (a third fewer LDS bytes per flop, and a higher clock) measured 11% slower: with
 // one wavefront per SIMD the matrix pipe idles at every wait.
 struct TileCfg {
-  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4;
+  static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, STAGES = 2;
 };
 // Segment tails of at most kTailRows rows (FWD, DGRAD): 128 x 512 tiles, the same
 // 128 x 64 wavefront tile with the 8 wavefronts side by side in N, a 160 KiB
@@ -835,9 +848,27 @@ struct TileCfg {
 // A 256 x 256 tile spends as many MFMAs on a tail of 1..128 rows as on a full one;
 // a 128 x 512 tile covers twice the columns for the same MFMAs.
 struct TailCfg {
-  static constexpr int BM = 128, BN = 512, WAVES_M = 1, WAVES_N = 8;
+  static constexpr int BM = 128, BN = 512, WAVES_M = 1, WAVES_N = 8, STAGES = 2;
 };
 constexpr int kTailRows = TailCfg::BM;
+// Small calls (FWD and DGRAD with under two rounds of full 256 x 256 tiles over the CUs;
+// the fused SwiGLU epilogue needs 64-column wavefront tiles and keeps the large ones):
+// most of their operand lines come from HBM, not from another workgroup's L2 fetch, and
+// one 64-deep step of lookahead leaves each step waiting for HBM. 128 x 128 tiles (8
+// wavefronts of 64 x 32) in a 4-stage ring of the same 128 KiB keep three steps in
+// flight and give the CUs four times as many tiles to balance. Every output element
+// gets the same MFMAs in the same k order as with the large tiles.
+struct SmallCfg {
+  static constexpr int BM = 128, BN = 128, WAVES_M = 2, WAVES_N = 4, STAGES = 4;
+};
+
+static int64_t full_tiles(const moonep_shape& s, int ncols) {
+  return int64_t(s.R) * s.S * s.K / TileCfg::BM * ((ncols + TileCfg::BN - 1) / TileCfg::BN);
+}
+
+static bool small_tiles(const moonep_shape& s, int ncols, int cus) {
+  return full_tiles(s, ncols) < 2 * int64_t(cus);
+}
 
 // Whether segment tails get their own launch. The split halves the MFMAs spent on
 // tails, but the tail launch waits for the full-tile launch; a GEMM of under four
@@ -845,22 +876,26 @@ constexpr int kTailRows = TailCfg::BM;
 // it saves (a layer of 32768 slots, H = 1024, H' = 512: 137 -> 101 us without it).
 // Either way every output element gets the same MFMAs in the same k order.
 static bool split_tails(const moonep_shape& s, int ncols, int cus) {
-  const int64_t full = int64_t(s.R) * s.S * s.K / TileCfg::BM *
-                       ((ncols + TileCfg::BN - 1) / TileCfg::BN);
-  return full >= 4 * int64_t(cus);
+  return full_tiles(s, ncols) >= 4 * int64_t(cus);
 }
 
 template <int OP, bool SWIGLU, typename C, bool STREAM_OUT = false>
 static void launch_cfg(const GemmArgs& g, int cus, hipStream_t strm) {
-  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU, STREAM_OUT>
+  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU, STREAM_OUT, C::STAGES>
       <<<cus, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
-// the full-tile list, then (FWD and DGRAD, when the tails are split off) the tail list
-// on the tail kernel
+// The full-tile list (on the small-tile kernel for a small call), then (FWD and DGRAD,
+// when the tails are split off) the tail list on the tail kernel.
 template <int OP, bool SWIGLU = false, bool STREAM_OUT = false>
 static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntails,
-                        bool tails_apart, int cus, hipStream_t strm) {
+                        bool tails_apart, bool small, int cus, hipStream_t strm) {
+  if constexpr (OP != MOONEP_WGRAD && !SWIGLU) {
+    if (small) {
+      launch_cfg<OP, SWIGLU, SmallCfg, STREAM_OUT>(g, cus, strm);
+      return;
+    }
+  }
   launch_cfg<OP, SWIGLU, TileCfg, STREAM_OUT>(g, cus, strm);
   if (OP != MOONEP_WGRAD && tails_apart) {
     g.tiles = tails;
@@ -915,9 +950,12 @@ static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const v
   const bool mtiled = bf16 && op != MOONEP_WGRAD;
   const int cus = device_cus();
   if (cus <= 0) return MOONEP_EHIP;
-  const bool tails_apart = mtiled && split_tails(s, op == MOONEP_DGRAD ? s.H : s.Hp, cus);
+  const int ncols = op == MOONEP_DGRAD ? s.H : s.Hp;
+  const bool small = mtiled && small_tiles(s, ncols, cus);
+  const bool tails_apart = mtiled && split_tails(s, ncols, cus);
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
-                                          mtiled ? TileCfg::BM : 0, tails_apart ? kTailRows : 0,
+                                          mtiled ? (small ? SmallCfg::BM : TileCfg::BM) : 0,
+                                          tails_apart ? kTailRows : 0,
                                           bf16 && op == MOONEP_WGRAD, w.tiles, w.ntiles,
                                           int(w.max_tiles), w.tails, w.ntails, int(w.max_tail));
   if (launch_status()) return MOONEP_EHIP;
@@ -925,11 +963,13 @@ static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const v
   if (bf16) {
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
                reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
-    if (op == MOONEP_FWD) launch_bf16<MOONEP_FWD>(g, w.tails, w.ntails, tails_apart, cus, strm);
+    if (op == MOONEP_FWD)
+      launch_bf16<MOONEP_FWD>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
     else if (op == MOONEP_DGRAD && s.Hp <= kStreamOutMaxK)
-      launch_bf16<MOONEP_DGRAD, false, true>(g, w.tails, w.ntails, tails_apart, cus, strm);
-    else if (op == MOONEP_DGRAD) launch_bf16<MOONEP_DGRAD>(g, w.tails, w.ntails, tails_apart, cus, strm);
-    else launch_bf16<MOONEP_WGRAD>(g, w.tails, w.ntails, false, cus, strm);
+      launch_bf16<MOONEP_DGRAD, false, true>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
+    else if (op == MOONEP_DGRAD)
+      launch_bf16<MOONEP_DGRAD>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
+    else launch_bf16<MOONEP_WGRAD>(g, w.tails, w.ntails, false, false, cus, strm);
   } else {
     const dim3 grid(64, 256);
     const float* af = static_cast<const float*>(a);
@@ -1054,7 +1094,7 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
     GemmArgs g{static_cast<const uint16_t*>(xp), static_cast<const uint16_t*>(w1_all), nullptr,
                nullptr, nullptr, tiles, ntiles, s.H, 2 * s.Hp, s.E,
                static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved)};
-    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, tails_apart, cus, strm);
+    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, tails_apart, false, cus, strm);
   } else {
     gemm_fp32_swiglu_kernel<<<dim3(64, 256), 256, 0, strm>>>(
         static_cast<const float*>(xp), static_cast<const float*>(w1_all),
