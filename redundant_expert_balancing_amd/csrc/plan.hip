@@ -28,14 +28,25 @@ namespace moonep {
 constexpr int kWavesPerBlock = 4;
 constexpr int kSolveThreads = 1024;
 
+// Inclusive scan across the 64 lanes of a wavefront with DPP (no LDS round trips):
+// Hillis-Steele over row shifts of 1, 2, 4 and 8 lanes builds the prefix inside each
+// 16-lane row (lanes shifted in from outside the row read 0); then lane 15's total is
+// broadcast into rows 1 and 3, and lane 31's into rows 2 and 3.
 __device__ inline int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
   return v;
+}
+
+// Exclusive scan across one wavefront; *total gets the wavefront sum.
+__device__ inline int wave_excl_scan(int v, int* total) {
+  const int incl = wave_incl_scan(v);
+  *total = __shfl(incl, 63, 64);
+  return incl - v;
 }
 
 // Exclusive scan across a 1024-thread block; *total gets the block sum.
@@ -197,17 +208,119 @@ __device__ inline void for_each_piece(const SolveArgs& a, const int* sm, const S
   if (x < y) f(p, e, x - off, y - off, -1);
 }
 
+// The donor tree of the solve kernel (rule and closed form where it is called). Run by
+// the whole block (scan and sync across all threads) or, when R <= 64, by one wavefront
+// alone: the same steps with wavefront scans and no block barriers.
+template <class Scan, class Sync>
+__device__ inline void donor_tree(const SolveArgs& a, int* sm, const SolveLds& L, int tid,
+                                  Scan scan, Sync sync) {
+  const int p = tid;
+  const bool in = p < a.R;
+  const int lp = in ? sm[L.L + p] : 0;
+  const int ishot = in && lp > a.SK, iscold = in && lp < a.SK;
+  int nhot, ncold, sx, sn;
+  const int hidx = scan(ishot, &nhot);
+  const int cidx = scan(iscold, &ncold);
+  const int hpre = scan(ishot ? lp - a.SK : 0, &sx);
+  const int cpre = scan(iscold ? a.SK - lp : 0, &sn);
+  if (ishot) {
+    sm[L.hot + hidx] = p;
+    sm[L.hsum + hidx] = hpre + (lp - a.SK);
+    sm[L.cfirst + hidx] = -1;
+    sm[L.clast + hidx] = -2;
+  }
+  if (iscold) {
+    sm[L.crank + cidx] = p;
+    sm[L.csum + cidx] = cpre + (a.SK - lp);
+  }
+  sync();
+  // cold j: its donor's hot index, by binary search over S
+  if (tid < ncold) {
+    const int dprev = tid > 0 ? sm[L.csum + tid - 1] : 0;
+    int lo = 0, hi = nhot - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sm[L.hsum + mid] > dprev) hi = mid; else lo = mid + 1;
+    }
+    sm[L.cdon + tid] = lo;
+  }
+  // hot i >= 1: the gift to hot i-1, by binary search over D
+  if (tid < nhot) {
+    int amt = 0;
+    if (tid > 0) {
+      const int sp = sm[L.hsum + tid - 1];
+      int lo = 0, hi = ncold;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sm[L.csum + mid] > sp) hi = mid; else lo = mid + 1;
+      }
+      const int dprev = lo > 0 ? sm[L.csum + lo - 1] : 0;
+      if (lo < ncold && dprev < sp) amt = sm[L.csum + lo] - sp;
+    }
+    sm[L.chain + tid] = amt;
+  }
+  sync();
+  // the run of cold ranks each donor gives to (cdon is non-decreasing in j)
+  if (tid < ncold) {
+    const int d = sm[L.cdon + tid];
+    if (tid == 0 || sm[L.cdon + tid - 1] != d) sm[L.cfirst + d] = tid;
+    if (tid == ncold - 1 || sm[L.cdon + tid + 1] != d) sm[L.clast + d] = tid;
+  }
+  sync();
+  // gift counts per donor rank, grouped by donor in ascending id
+  int cnt = 0, chain_amt = 0, first = -1, last = -2;
+  if (ishot) {
+    chain_amt = sm[L.chain + hidx];
+    first = sm[L.cfirst + hidx];
+    last = sm[L.clast + hidx];
+    cnt = (chain_amt > 0) + (last - first + 1);
+  }
+  int ngift;
+  const int base = scan(cnt, &ngift);
+  if (in) sm[L.dptr + p] = base;
+  if (tid == 0) {
+    sm[L.dptr + a.R] = ngift;
+    sm[L.misc] = ngift;
+  }
+  if (in) {
+    int given = 0;
+    if (ishot) {
+      const int d0 = first > 0 ? sm[L.csum + first - 1] : 0;
+      given = chain_amt + (last >= first ? sm[L.csum + last] - d0 : 0);
+      if (chain_amt > 0) {
+        sm[L.gchild + base] = sm[L.hot + hidx - 1];
+        sm[L.gamt + base] = chain_amt;
+        sm[L.glo + base] = 0;
+      }
+    }
+    sm[L.homestart + p] = given;
+  }
+  sync();
+  if (tid < ncold) {
+    const int i = sm[L.cdon + tid];
+    const int d = sm[L.hot + i];
+    const int ch = sm[L.chain + i];
+    const int first_j = sm[L.cfirst + i];
+    const int k = sm[L.dptr + d] + (ch > 0) + (tid - first_j);
+    const int dprev = tid > 0 ? sm[L.csum + tid - 1] : 0;
+    const int dfirst = first_j > 0 ? sm[L.csum + first_j - 1] : 0;
+    sm[L.gchild + k] = sm[L.crank + tid];
+    sm[L.gamt + k] = sm[L.csum + tid] - dprev;
+    sm[L.glo + k] = ch + (dprev - dfirst);
+  }
+}
+
 __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) {
   extern __shared__ int sm[];
   const SolveLds L(a.R, a.E, a.B);
   const int tid = threadIdx.x;
   const int EB = a.E + a.B;
 
-  __shared__ unsigned long long s_total;
+  __shared__ unsigned int s_total;
   if (tid == 0) s_total = 0;
   __syncthreads();
   // T[e]: sum of the partition totals, which become the prefix over partitions
-  unsigned long long sum = 0;
+  unsigned int sum = 0;   // at most N*K < 2^31: every slot counts once, and only valid ids
   for (int e = tid; e < a.E; e += kSolveThreads) {
     int run = 0;
     for (int p0 = 0; p0 < a.npart; p0 += 8) {
@@ -223,34 +336,59 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
     sm[L.T + e] = run;
     sum += run;
   }
-  atomicAdd(&s_total, sum);
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  if ((tid & 63) == 0 && sum) atomicAdd(&s_total, sum);
   for (int i = tid; i < a.R * EB; i += kSolveThreads) sm[L.rowlen + i] = 0;
   for (int i = tid; i < a.R * a.B; i += kSolveThreads) a.replica[i] = -1;
   __syncthreads();
 
-  if (s_total != (unsigned long long)a.NK) {  // an id outside [0,E): publish an empty plan
+  if (s_total != (unsigned int)a.NK) {  // an id outside [0,E): publish an empty plan
     for (int i = tid; i < a.R * (EB + 1); i += kSolveThreads) a.cu[i] = 0;
     for (int i = tid; i <= a.E; i += kSolveThreads) a.piece_ptr[i] = 0;
     if (tid == 0) a.flags[kFlagPlanValid] = 0;
     return;
   }
 
-  // rank loads L_p
-  for (int p = tid; p < a.R; p += kSolveThreads) {
-    int s = 0;
-    for (int e = p * a.G; e < (p + 1) * a.G; ++e) s += sm[L.T + e];
-    sm[L.L + p] = s;
-  }
-  // layout of each group: position by (T desc, e asc)
-  for (int e = tid; e < a.E; e += kSolveThreads) {
-    const int p = e / a.G, te = sm[L.T + e];
-    int pos = 0;
-    for (int e2 = p * a.G; e2 < (p + 1) * a.G; ++e2) {
-      const int t2 = sm[L.T + e2];
-      pos += (t2 > te) || (t2 == te && e2 < e);
+  // rank loads L_p, and each group's layout: an expert's position by (T desc, e asc) is
+  // the number of its group's experts that sort before it
+  if (a.G <= 64) {
+    // a wavefront per group, a lane per expert: the load by a shuffle reduction, the
+    // positions by one pass over the group's T read lane by lane
+    const int lane = tid & 63, w = tid >> 6;
+    for (int p = w; p < a.R; p += kSolveThreads / 64) {
+      const int e = p * a.G + lane;
+      const int te = lane < a.G ? sm[L.T + e] : 0;
+      int s = te;
+#pragma unroll
+      for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+      if (lane == 0) sm[L.L + p] = s;
+      int pos = 0;
+      for (int j = 0; j < a.G; ++j) {
+        const int tj = __builtin_amdgcn_readlane(te, j);
+        pos += (tj > te) || (tj == te && j < lane);
+      }
+      if (lane < a.G) {
+        sm[L.seqpos + e] = pos;
+        sm[L.seq + p * a.G + pos] = e;
+      }
     }
-    sm[L.seqpos + e] = pos;
-    sm[L.seq + p * a.G + pos] = e;
+  } else {
+    for (int p = tid; p < a.R; p += kSolveThreads) {
+      int s = 0;
+      for (int e = p * a.G; e < (p + 1) * a.G; ++e) s += sm[L.T + e];
+      sm[L.L + p] = s;
+    }
+    for (int e = tid; e < a.E; e += kSolveThreads) {
+      const int p = e / a.G, te = sm[L.T + e];
+      int pos = 0;
+      for (int e2 = p * a.G; e2 < (p + 1) * a.G; ++e2) {
+        const int t2 = sm[L.T + e2];
+        pos += (t2 > te) || (t2 == te && e2 < e);
+      }
+      sm[L.seqpos + e] = pos;
+      sm[L.seq + p * a.G + pos] = e;
+    }
   }
   __syncthreads();
   // off(e): T summed over the experts before e in its group's layout, one
@@ -280,101 +418,18 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
   //   and that gift is made before any of hot i's gifts to cold ranks.
   // A donor's gift list is therefore its gift to the previous hot rank (if any),
   // then its cold ranks in ascending id; consecutive layout ranges from 0 follow.
-  {
-    const int p = tid;
-    const bool in = p < a.R;
-    const int lp = in ? sm[L.L + p] : 0;
-    const int ishot = in && lp > a.SK, iscold = in && lp < a.SK;
-    int nhot, ncold, sx, sn;
-    const int hidx = block_excl_scan(ishot, sm + L.swave, &nhot);
-    const int cidx = block_excl_scan(iscold, sm + L.swave, &ncold);
-    const int hpre = block_excl_scan(ishot ? lp - a.SK : 0, sm + L.swave, &sx);
-    const int cpre = block_excl_scan(iscold ? a.SK - lp : 0, sm + L.swave, &sn);
-    if (ishot) {
-      sm[L.hot + hidx] = p;
-      sm[L.hsum + hidx] = hpre + (lp - a.SK);
-      sm[L.cfirst + hidx] = -1;
-      sm[L.clast + hidx] = -2;
-    }
-    if (iscold) {
-      sm[L.crank + cidx] = p;
-      sm[L.csum + cidx] = cpre + (a.SK - lp);
-    }
-    __syncthreads();
-    // cold j: its donor's hot index, by binary search over S
-    if (tid < ncold) {
-      const int dprev = tid > 0 ? sm[L.csum + tid - 1] : 0;
-      int lo = 0, hi = nhot - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sm[L.hsum + mid] > dprev) hi = mid; else lo = mid + 1;
-      }
-      sm[L.cdon + tid] = lo;
-    }
-    // hot i >= 1: the gift to hot i-1, by binary search over D
-    if (tid < nhot) {
-      int amt = 0;
-      if (tid > 0) {
-        const int sp = sm[L.hsum + tid - 1];
-        int lo = 0, hi = ncold;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (sm[L.csum + mid] > sp) hi = mid; else lo = mid + 1;
-        }
-        const int dprev = lo > 0 ? sm[L.csum + lo - 1] : 0;
-        if (lo < ncold && dprev < sp) amt = sm[L.csum + lo] - sp;
-      }
-      sm[L.chain + tid] = amt;
-    }
-    __syncthreads();
-    // the run of cold ranks each donor gives to (cdon is non-decreasing in j)
-    if (tid < ncold) {
-      const int d = sm[L.cdon + tid];
-      if (tid == 0 || sm[L.cdon + tid - 1] != d) sm[L.cfirst + d] = tid;
-      if (tid == ncold - 1 || sm[L.cdon + tid + 1] != d) sm[L.clast + d] = tid;
-    }
-    __syncthreads();
-    // gift counts per donor rank, grouped by donor in ascending id
-    int cnt = 0, chain_amt = 0, first = -1, last = -2;
-    if (ishot) {
-      chain_amt = sm[L.chain + hidx];
-      first = sm[L.cfirst + hidx];
-      last = sm[L.clast + hidx];
-      cnt = (chain_amt > 0) + (last - first + 1);
-    }
-    int ngift;
-    const int base = block_excl_scan(cnt, sm + L.swave, &ngift);
-    if (in) sm[L.dptr + p] = base;
-    if (tid == 0) {
-      sm[L.dptr + a.R] = ngift;
-      sm[L.misc] = ngift;
-    }
-    if (in) {
-      int given = 0;
-      if (ishot) {
-        const int d0 = first > 0 ? sm[L.csum + first - 1] : 0;
-        given = chain_amt + (last >= first ? sm[L.csum + last] - d0 : 0);
-        if (chain_amt > 0) {
-          sm[L.gchild + base] = sm[L.hot + hidx - 1];
-          sm[L.gamt + base] = chain_amt;
-          sm[L.glo + base] = 0;
-        }
-      }
-      sm[L.homestart + p] = given;
-    }
-    __syncthreads();
-    if (tid < ncold) {
-      const int i = sm[L.cdon + tid];
-      const int d = sm[L.hot + i];
-      const int ch = sm[L.chain + i];
-      const int first_j = sm[L.cfirst + i];
-      const int k = sm[L.dptr + d] + (ch > 0) + (tid - first_j);
-      const int dprev = tid > 0 ? sm[L.csum + tid - 1] : 0;
-      const int dfirst = first_j > 0 ? sm[L.csum + first_j - 1] : 0;
-      sm[L.gchild + k] = sm[L.crank + tid];
-      sm[L.gamt + k] = sm[L.csum + tid] - dprev;
-      sm[L.glo + k] = ch + (dprev - dfirst);
-    }
+  if (a.R <= 64) {
+    if (tid < 64)
+      donor_tree(a, sm, L, tid, [](int v, int* t) { return wave_excl_scan(v, t); }, []() {
+        // a wavefront's LDS accesses run in program order: keep the compiler from
+        // moving them across the steps
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      });
+  } else {
+    donor_tree(a, sm, L, tid,
+               [&](int v, int* t) { return block_excl_scan(v, sm + L.swave, t); },
+               []() { __syncthreads(); });
   }
   __syncthreads();
 
