@@ -31,6 +31,9 @@
  *     every output of expert compute are float32.
  *   - A call returns MOONEP_OK or a negative status before launching anything
  *     when its arguments are invalid (see moonep_strerror).
+ *   - A call with nothing to move (S = 0 for dispatch, combine and the SwiGLU
+ *     calls; B = 0 for prefetch and reduce_grad) returns MOONEP_OK once the shape
+ *     is valid, without reading its pointers, which may then be NULL.
  *   - W_all is the [E+B,H,Hp] expert weight view of every rank at once: one
  *     tensor of E + R*B rows [E+R*B, H, Hp]. Rank q's row i is W_all[i] for
  *     i < E (the home experts, shared by all ranks) and W_all[E + q*B + (i-E)]
@@ -74,10 +77,12 @@ const char* moonep_strerror(int status);
 
 /*
  * Validate a layer shape. Rules [maestro "The memory contract"; spaxe 7-8]:
- *   E % R == 0; 0 <= B <= E/R; training needs B == E/R (replicas come from at
- *   most one remote home group, so every touched expert is local); inference
- *   allows B < E/R. 1 <= K <= min(E, 32); S >= 0; R*S*K < 2^31;
- *   H, Hp multiples of 8 (bf16) or 4 (fp32).
+ *   R, E >= 1 and E % R == 0; 0 <= B <= E/R; training needs B == E/R (replicas
+ *   come from at most one remote home group, so every touched expert is local);
+ *   inference allows B < E/R. 1 <= K <= min(E, 32); S >= 0; R*S*K < 2^31;
+ *   H, Hp positive multiples of 8 (bf16) or 4 (fp32); mode and dtype one of
+ *   their enum values. A shape breaking these gives MOONEP_EINVAL; one that keeps
+ *   them but passes a limit below gives MOONEP_ELIMIT.
  * Size limits (MOONEP_ELIMIT): E <= 1024, R <= 1024, R*(E+B+1) <= 8192,
  *   R*B <= 4096.
  */

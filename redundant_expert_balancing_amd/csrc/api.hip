@@ -15,7 +15,10 @@ int validate(const moonep_shape* s) {
   // training: B = E/R, so a rank's replicas (all from one remote home group) fit
   if (s->mode == MOONEP_TRAIN && s->B != G) return MOONEP_EINVAL;
   if (s->K > s->E || s->K > 32) return MOONEP_EINVAL;
-  if (int64_t(s->R) * s->S * s->K >= (int64_t(1) << 31)) return MOONEP_EINVAL;
+  // R*S*K < 2^31 without forming a product that can overflow: K <= 32, so R*K fits in
+  // 64 bits, and R*K*S >= 2^31 exactly when R*K > floor((2^31 - 1) / S)
+  const int64_t rk = int64_t(s->R) * s->K;
+  if (s->S > 0 && rk > int64_t(INT32_MAX) / s->S) return MOONEP_EINVAL;
   const int vec = s->dtype == MOONEP_BF16 ? 8 : 4;  // elements per 16-byte vector
   if (s->H < vec || s->Hp < vec || s->H % vec || s->Hp % vec) return MOONEP_EINVAL;
   if (s->E > 1024 || s->R > 1024) return MOONEP_ELIMIT;
