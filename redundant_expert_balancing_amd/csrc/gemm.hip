@@ -536,24 +536,67 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 #pragma unroll
       for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 16, ks, lane);
     };
+    auto mfma = [&](int buf, int i, int j) {
+      if constexpr (SWAP)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
+    // MFMA order inside a half step. Row-outer order frees each A fragment after its
+    // row, but every B fragment only in the last row, so all the B refills are issued at
+    // the end and the next half needs them at once. The two wavefronts of a SIMD do not
+    // share the matrix pipe evenly: the older one reaches the barrier first and waits
+    // there about a third of each step (s_memtime probe), and the other, running alone,
+    // stalls on those refills. Two column blocks (every row with the first FN/2 columns,
+    // then every row with the rest) free the first block's B fragments for refill under
+    // the second block; the second block's are needed only halfway through the next half,
+    // and each A fragment only at its row in the next half's first block. Every
+    // accumulator keeps its k order, so results are bit-identical. Measured: FWD at
+    // H = 7168, H' = 2048 13.70 -> 13.44 ms, at H = 4096, H' = 1408 -2.5%; DGRAD unchanged.
+    // WGRAD, whose A refills are transposed reads too, has more refills than the second
+    // block has MFMAs and keeps row-outer order (the split spread over its MFMAs measured
+    // no gain there).
+    constexpr bool SPLIT = FN >= 4 && FN % 2 == 0 &&
+                           FM * OA::READS + (FN / 2) * OB::READS <= FM * FN / 2;
     auto mfmas = [&](int buf) {
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          if constexpr (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = jb * (FN / 2); j < (jb + 1) * (FN / 2); ++j) mfma(buf, i, j);
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mfma(buf, i, j);
+      }
     };
     // LDS reads per substep: one per k-contiguous fragment, two per transposed one
     constexpr int READS = FM * OA::READS + FN * OB::READS;
     constexpr int PER_READ = (FM * FN) / READS > 0 ? (FM * FN) / READS : 1;
     auto interleave = [&]() {
+      if constexpr (SPLIT) {
+        constexpr int HALFM = FM * FN / 2;
+        constexpr int EARLY = FM * OA::READS + (FN / 2) * OB::READS;
+        // no refill fits under the first block; under the second, one LDS read after each
+        // MFMA for the refills freed so far, and the last block's B refills at the end
+        __builtin_amdgcn_sched_group_barrier(0x008, HALFM, 0);      // first column block
 #pragma unroll
-      for (int q = 0; q < READS; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, PER_READ, 0);   // MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one LDS read
+        for (int q = 0; q < EARLY; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+        }
+        if constexpr (HALFM > EARLY)
+          __builtin_amdgcn_sched_group_barrier(0x008, HALFM - EARLY, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, READS - EARLY, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < READS; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER_READ, 0);   // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one LDS read
+        }
       }
     };
     // step 0 landed (the later steps of the ring may still be in flight)
