@@ -368,10 +368,22 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   static_assert(!SWIGLU || (OP == MOONEP_FWD && FN % 4 == 0 && kSwigluBlock == 32),
                 "SwiGLU epilogue: a wavefront holds whole (gate, up) 32-column block pairs");
   // A stored k-contiguous except in WGRAD; B stored n-contiguous except in DGRAD
-  using OA = typename std::conditional<OP == MOONEP_WGRAD, OpMN<BM, NW>, OpK<BM, NW>>::type;
-  using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, NW>, OpMN<BN, NW>>::type;
+  // Wavefronts that issue the DMAs. The two wavefronts on each SIMD (w and w + NW/2)
+  // share its matrix pipe unevenly: with every wavefront issuing an equal share, the
+  // older one reaches each barrier early and waits there about a third of the step
+  // (s_memtime probe), and the other is on the critical path. In FWD and WGRAD the
+  // older ones (w < NW/2) issue every DMA, twice their share, and the others issue none
+  // and never wait on the vector-memory counter; the barrier still follows every
+  // issuing wavefront's wait for its own share. Bit-identical. A/B on one box: FWD at
+  // H = 7168, H' = 2048 13.54 -> 13.17 ms, at H = 4096, H' = 1536 -3 to -4%, WGRAD at
+  // H = 4096, H' = 1408 -4%; DGRAD measured no change and keeps all wavefronts. Issue
+  // counts in between (one operand from w < NW/2, the other from all: 12 and 4 per step)
+  // were 6-10% slower than the equal split, so what pays is wavefronts free of DMA waits.
+  constexpr int DW = OP == MOONEP_DGRAD ? NW : NW / 2;
+  using OA = typename std::conditional<OP == MOONEP_WGRAD, OpMN<BM, DW>, OpK<BM, DW>>::type;
+  using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, DW>, OpMN<BN, DW>>::type;
+  constexpr int DMA_PER_STEP = OA::PER_WAVE + OB::PER_WAVE;   // per issuing wavefront
   constexpr int STAGE = OA::BYTES + OB::BYTES;
-  constexpr int DMA_PER_STEP = OA::PER_WAVE + OB::PER_WAVE;
   static_assert(STAGES >= 2 && (STAGES & (STAGES - 1)) == 0, "LDS ring depth: a power of two");
   __shared__ __align__(1024) char smem[STAGES * STAGE];
 
@@ -444,6 +456,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   };
   // issue the DMAs of k-step kt of task t into the ring stage at LDS address st
   auto issue_task = [&](const Task& t, int kt, uint32_t st) {
+    if (wid >= DW) return;   // uniform per wavefront
     const int k0 = kt * kBK;
     const TileEntry& te = t.te;
     const int m0 = t.m0, n0 = t.n0, rows_valid = t.rows_valid, cols_valid = t.cols_valid;
@@ -505,6 +518,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       if (k < kiters) issue(k);
     // wait until at most n later steps of this wavefront's DMAs are in flight
     auto wait_steps = [&](int n) {
+      if (wid >= DW) return;   // no DMAs of its own
       if constexpr (STAGES > 3) {
         if (n >= 3) { wait_vm<3 * DMA_PER_STEP>(); return; }
       }
