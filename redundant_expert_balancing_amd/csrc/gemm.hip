@@ -502,275 +502,293 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     auto stage = [&](int kt) { return uint32_t((base + kt) & (STAGES - 1)) * STAGE; };
     auto issue = [&](int kt) { issue_task(cur, kt, lds0 + stage(kt)); };
 
-    floatx4_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
-
-    // every wavefront has finished reading the ring (previous tile) before refilling it
-    __syncthreads();
-    if (!step0_issued) issue(0);
-#pragma unroll
-    for (int k = 1; k < STAGES; ++k)
-      if (k < kiters) issue(k);
-    // wait until at most n later steps of this wavefront's DMAs are in flight
-    auto wait_steps = [&](int n) {
-      if (wid >= DW) return;   // no DMAs of its own
-      if constexpr (STAGES > 3) {
-        if (n >= 3) { wait_vm<3 * DMA_PER_STEP>(); return; }
-      }
-      if constexpr (STAGES > 2) {
-        if (n == 2) { wait_vm<2 * DMA_PER_STEP>(); return; }
-      }
-      if (n == 1) wait_vm<DMA_PER_STEP>();
-      else wait_vm<0>();
-    };
-
-    // The fragments of half a step (one 32-deep substep: FM + FN operands of 4
-    // registers) live in registers: a whole step's would need 96 registers beside
-    // the 128 accumulators and spills. Step kt:
-    //   first half   MFMAs of substep 0; its registers refilled with substep 1 of
-    //                the same step (the last reads of its stage)
-    //   barrier      step kt+1 is visible to every wavefront, and every read of
-    //                stage kt % 2 has completed, so step kt+2 is issued into it
-    //   second half  MFMAs of substep 1; registers refilled with substep 0 of
-    //                step kt+1
-    // LDS reads are spread between the MFMAs, so they run under the MFMAs and the
-    // MFMA pipe never drains at the barrier.
-    constexpr int KS = kBK / 32;
-    constexpr int HALF = KS / 2;
-    bf16x8_t fa[HALF][FM], fb[HALF][FN];
-    auto load = [&](int kt, int ks, int buf) {
-      const char* st = smem + stage(kt);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[buf][i] = OA::frag(st, wm * WM + i * 16, ks, lane);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 16, ks, lane);
-    };
-    auto mfma = [&](int buf, int i, int j) {
-      if constexpr (SWAP)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-    };
-    // MFMA order inside a half step. Row-outer order frees each A fragment after its
-    // row, but every B fragment only in the last row, so all the B refills are issued at
-    // the end and the next half needs them at once. The two wavefronts of a SIMD do not
-    // share the matrix pipe evenly: the older one reaches the barrier first and waits
-    // there about a third of each step (s_memtime probe), and the other, running alone,
-    // stalls on those refills. Two column blocks (every row with the first FN/2 columns,
-    // then every row with the rest) free the first block's B fragments for refill under
-    // the second block; the second block's are needed only halfway through the next half,
-    // and each A fragment only at its row in the next half's first block. Every
-    // accumulator keeps its k order, so results are bit-identical. Measured: FWD at
-    // H = 7168, H' = 2048 13.70 -> 13.44 ms, at H = 4096, H' = 1408 -2.5%; DGRAD unchanged.
-    // WGRAD, whose A refills are transposed reads too, has more refills than the second
-    // block has MFMAs and keeps row-outer order (the split spread over its MFMAs measured
-    // no gain there).
-    constexpr bool SPLIT = FN >= 4 && FN % 2 == 0 &&
-                           FM * OA::READS + (FN / 2) * OB::READS <= FM * FN / 2;
-    auto mfmas = [&](int buf) {
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = jb * (FN / 2); j < (jb + 1) * (FN / 2); ++j) mfma(buf, i, j);
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) mfma(buf, i, j);
-      }
-    };
-    // LDS reads per substep: one per k-contiguous fragment, two per transposed one
-    constexpr int READS = FM * OA::READS + FN * OB::READS;
-    constexpr int PER_READ = (FM * FN) / READS > 0 ? (FM * FN) / READS : 1;
-    auto interleave = [&]() {
-      if constexpr (SPLIT) {
-        constexpr int HALFM = FM * FN / 2;
-        constexpr int EARLY = FM * OA::READS + (FN / 2) * OB::READS;
-        // no refill fits under the first block; under the second, one LDS read after each
-        // MFMA for the refills freed so far, and the last block's B refills at the end
-        __builtin_amdgcn_sched_group_barrier(0x008, HALFM, 0);      // first column block
-#pragma unroll
-        for (int q = 0; q < EARLY; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
-        }
-        if constexpr (HALFM > EARLY)
-          __builtin_amdgcn_sched_group_barrier(0x008, HALFM - EARLY, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, READS - EARLY, 0);
-      } else {
-#pragma unroll
-        for (int q = 0; q < READS; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, PER_READ, 0);   // MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one LDS read
-        }
-      }
-    };
-    // step 0 landed (the later steps of the ring may still be in flight)
-    wait_steps(min(STAGES, kiters) - 1);
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < HALF; ++h) load(0, h, h);
-    for (int kt = 0; kt < kiters; ++kt) {
-      const bool more = kt + 1 < kiters;
-#pragma unroll
-      for (int h = 0; h < HALF; ++h) {
-        mfmas(h);
-        load(kt, HALF + h, h);
-        interleave();
-      }
-      // this wavefront's DMAs of step kt+1 (steps up to kt+STAGES-1 may be in flight)
-      if (more) wait_steps(min(kt + STAGES - 1, kiters - 1) - (kt + 1));
-      __syncthreads();
-      if (kt + STAGES < kiters) issue(kt + STAGES);
-      else if (!more && has_next) issue_task(task_at(tau + G), 0, lds0 + stage(kt));
-#pragma unroll
-      for (int h = 0; h < HALF; ++h) {
-        mfmas(h);
-        // after the last step: read a stage with no DMA in flight into it (in bounds,
-        // values unused): this step's, or the other one when the next tile's step 0
-        // is on its way into this one
-        load(more || NEXT_STEP0 ? kt + 1 : kt, h, h);
-        interleave();
-      }
-    }
-    if constexpr (NEXT_STEP0) {
-      step0_issued = has_next;
-      base = (base + kiters - 1) & 1;
-    }
-
-    // epilogue: lane holds column lane % 16 and rows 4 * (lane / 16) + r (r = 0..3)
-    // of each 16 x 16 block; rows past rows_valid fall outside the range.
-    const int r16 = lane & 15;
-    const uint32_t lane_rows = uint32_t(wm * WM + (lane >> 4) * 4);
-    if constexpr (SWIGLU) {
-      // in each 64-column group jp of the wavefront, blocks 4jp, 4jp+1 hold the gate
-      // and blocks 4jp+2, 4jp+3 the up value of intermediate columns
-      // n0/2 + wn*WN/2 + jp*32 + (0..31); a partial tile ends on a 64-column boundary,
-      // so each group is all in or all out
-      const int hact = g.Hp / 2;
-      const int64_t row0 = int64_t(te.rowbase) + m0;
-      const __amdgpu_buffer_rsrc_t ars =
-          make_rsrc(g.act + row0 * hact + n0 / 2, clamp_bytes(int64_t(rows_valid) * hact * 2));
-      const uint32_t arow = lane_rows * hact * 2;
-      uint32_t la[FN / 4];
-#pragma unroll
-      for (int jp = 0; jp < FN / 4; ++jp)
-        la[jp] = wn * WN + jp * 64 < cols_valid
-                     ? arow + uint32_t(wn * (WN / 2) + jp * kSwigluBlock + r16) * 2
-                     : kOffNone;
+    // the tile's MFMAs, ring and epilogue for a wavefront of FM 16-row fragments whose
+    // rows start at row0 of the tile
+    auto tile = [&](auto fm_c, int row0) {
+      constexpr int FM = decltype(fm_c)::value;
+      floatx4_t acc[FM][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t rowoff = uint32_t(i * 16 + r) * hact * 2;
-#pragma unroll
-          for (int jp = 0; jp < FN / 4; ++jp)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float v = swiglu_f32(acc[i][4 * jp + h][r], acc[i][4 * jp + 2 + h][r]);
-              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
-                                                    la[jp] + rowoff + h * 32, 0, 0);
-            }
-        }
-      if (g.h_saved) {
-        const __amdgpu_buffer_rsrc_t hrs = make_rsrc(
-            g.h_saved + row0 * g.Hp + n0, clamp_bytes(int64_t(rows_valid) * g.Hp * 2));
-        const uint32_t hrow = lane_rows * g.Hp * 2;
-        uint32_t lh[FN];
-#pragma unroll
         for (int j = 0; j < FN; ++j)
-          lh[j] = wn * WN + (j / 4) * 64 < cols_valid ? hrow + uint32_t(wn * WN + j * 16 + r16) * 2
-                                                      : kOffNone;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+
+      // every wavefront has finished reading the ring (previous tile) before refilling it
+      __syncthreads();
+      if (!step0_issued) issue(0);
+#pragma unroll
+      for (int k = 1; k < STAGES; ++k)
+        if (k < kiters) issue(k);
+      // wait until at most n later steps of this wavefront's DMAs are in flight
+      auto wait_steps = [&](int n) {
+        if (wid >= DW) return;   // no DMAs of its own
+        if constexpr (STAGES > 3) {
+          if (n >= 3) { wait_vm<3 * DMA_PER_STEP>(); return; }
+        }
+        if constexpr (STAGES > 2) {
+          if (n == 2) { wait_vm<2 * DMA_PER_STEP>(); return; }
+        }
+        if (n == 1) wait_vm<DMA_PER_STEP>();
+        else wait_vm<0>();
+      };
+
+      // The fragments of half a step (one 32-deep substep: FM + FN operands of 4
+      // registers) live in registers: a whole step's would need 96 registers beside
+      // the 128 accumulators and spills. Step kt:
+      //   first half   MFMAs of substep 0; its registers refilled with substep 1 of
+      //                the same step (the last reads of its stage)
+      //   barrier      step kt+1 is visible to every wavefront, and every read of
+      //                stage kt % 2 has completed, so step kt+2 is issued into it
+      //   second half  MFMAs of substep 1; registers refilled with substep 0 of
+      //                step kt+1
+      // LDS reads are spread between the MFMAs, so they run under the MFMAs and the
+      // MFMA pipe never drains at the barrier.
+      constexpr int KS = kBK / 32;
+      constexpr int HALF = KS / 2;
+      bf16x8_t fa[HALF][FM], fb[HALF][FN];
+      auto load = [&](int kt, int ks, int buf) {
+        const char* st = smem + stage(kt);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = OA::frag(st, row0 + i * 16, ks, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 16, ks, lane);
+      };
+      auto mfma = [&](int buf, int i, int j) {
+        if constexpr (SWAP)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+      };
+      // MFMA order inside a half step. Row-outer order frees each A fragment after its
+      // row, but every B fragment only in the last row, so all the B refills are issued at
+      // the end and the next half needs them at once. The two wavefronts of a SIMD do not
+      // share the matrix pipe evenly: the older one reaches the barrier first and waits
+      // there about a third of each step (s_memtime probe), and the other, running alone,
+      // stalls on those refills. Two column blocks (every row with the first FN/2 columns,
+      // then every row with the rest) free the first block's B fragments for refill under
+      // the second block; the second block's are needed only halfway through the next half,
+      // and each A fragment only at its row in the next half's first block. Every
+      // accumulator keeps its k order, so results are bit-identical. Measured: FWD at
+      // H = 7168, H' = 2048 13.70 -> 13.44 ms, at H = 4096, H' = 1408 -2.5%; DGRAD unchanged.
+      // WGRAD, whose A refills are transposed reads too, has more refills than the second
+      // block has MFMAs and keeps row-outer order (the split spread over its MFMAs measured
+      // no gain there).
+      constexpr bool SPLIT = FN >= 4 && FN % 2 == 0 &&
+                             FM * OA::READS + (FN / 2) * OB::READS <= FM * FN / 2;
+      auto mfmas = [&](int buf) {
+        if constexpr (SPLIT) {
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = jb * (FN / 2); j < (jb + 1) * (FN / 2); ++j) mfma(buf, i, j);
+        } else {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) mfma(buf, i, j);
+        }
+      };
+      // LDS reads per substep: one per k-contiguous fragment, two per transposed one
+      constexpr int READS = FM * OA::READS + FN * OB::READS;
+      constexpr int PER_READ = (FM * FN) / READS > 0 ? (FM * FN) / READS : 1;
+      auto interleave = [&]() {
+        if constexpr (SPLIT) {
+          constexpr int HALFM = FM * FN / 2;
+          constexpr int EARLY = FM * OA::READS + (FN / 2) * OB::READS;
+          // no refill fits under the first block; under the second, one LDS read after each
+          // MFMA for the refills freed so far, and the last block's B refills at the end
+          __builtin_amdgcn_sched_group_barrier(0x008, HALFM, 0);      // first column block
+#pragma unroll
+          for (int q = 0; q < EARLY; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+          }
+          if constexpr (HALFM > EARLY)
+            __builtin_amdgcn_sched_group_barrier(0x008, HALFM - EARLY, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, READS - EARLY, 0);
+        } else {
+#pragma unroll
+          for (int q = 0; q < READS; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PER_READ, 0);   // MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // one LDS read
+          }
+        }
+      };
+      // step 0 landed (the later steps of the ring may still be in flight)
+      wait_steps(min(STAGES, kiters) - 1);
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < HALF; ++h) load(0, h, h);
+      for (int kt = 0; kt < kiters; ++kt) {
+        const bool more = kt + 1 < kiters;
+#pragma unroll
+        for (int h = 0; h < HALF; ++h) {
+          mfmas(h);
+          load(kt, HALF + h, h);
+          interleave();
+        }
+        // this wavefront's DMAs of step kt+1 (steps up to kt+STAGES-1 may be in flight)
+        if (more) wait_steps(min(kt + STAGES - 1, kiters - 1) - (kt + 1));
+        __syncthreads();
+        if (kt + STAGES < kiters) issue(kt + STAGES);
+        else if (!more && has_next) issue_task(task_at(tau + G), 0, lds0 + stage(kt));
+#pragma unroll
+        for (int h = 0; h < HALF; ++h) {
+          mfmas(h);
+          // after the last step: read a stage with no DMA in flight into it (in bounds,
+          // values unused): this step's, or the other one when the next tile's step 0
+          // is on its way into this one
+          load(more || NEXT_STEP0 ? kt + 1 : kt, h, h);
+          interleave();
+        }
+      }
+      if constexpr (NEXT_STEP0) {
+        step0_issued = has_next;
+        base = (base + kiters - 1) & 1;
+      }
+
+      // epilogue: lane holds column lane % 16 and rows 4 * (lane / 16) + r (r = 0..3)
+      // of each 16 x 16 block; rows past rows_valid fall outside the range.
+      const int r16 = lane & 15;
+      const uint32_t lane_rows = uint32_t(row0 + (lane >> 4) * 4);
+      if constexpr (SWIGLU) {
+        // in each 64-column group jp of the wavefront, blocks 4jp, 4jp+1 hold the gate
+        // and blocks 4jp+2, 4jp+3 the up value of intermediate columns
+        // n0/2 + wn*WN/2 + jp*32 + (0..31); a partial tile ends on a 64-column boundary,
+        // so each group is all in or all out
+        const int hact = g.Hp / 2;
+        const int64_t row0 = int64_t(te.rowbase) + m0;
+        const __amdgpu_buffer_rsrc_t ars =
+            make_rsrc(g.act + row0 * hact + n0 / 2, clamp_bytes(int64_t(rows_valid) * hact * 2));
+        const uint32_t arow = lane_rows * hact * 2;
+        uint32_t la[FN / 4];
+#pragma unroll
+        for (int jp = 0; jp < FN / 4; ++jp)
+          la[jp] = wn * WN + jp * 64 < cols_valid
+                       ? arow + uint32_t(wn * (WN / 2) + jp * kSwigluBlock + r16) * 2
+                       : kOffNone;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t rowoff = uint32_t(i * 16 + r) * g.Hp * 2;
+            const uint32_t rowoff = uint32_t(i * 16 + r) * hact * 2;
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][r]),
-                                                    hrs, lh[j] + rowoff, 0, 0);
+            for (int jp = 0; jp < FN / 4; ++jp)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const float v = swiglu_f32(acc[i][4 * jp + h][r], acc[i][4 * jp + 2 + h][r]);
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(v), ars,
+                                                      la[jp] + rowoff + h * 32, 0, 0);
+              }
           }
+        if (g.h_saved) {
+          const __amdgpu_buffer_rsrc_t hrs = make_rsrc(
+              g.h_saved + row0 * g.Hp + n0, clamp_bytes(int64_t(rows_valid) * g.Hp * 2));
+          const uint32_t hrow = lane_rows * g.Hp * 2;
+          uint32_t lh[FN];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            lh[j] = wn * WN + (j / 4) * 64 < cols_valid ? hrow + uint32_t(wn * WN + j * 16 + r16) * 2
+                                                        : kOffNone;
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t rowoff = uint32_t(i * 16 + r) * g.Hp * 2;
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne_bits(acc[i][j][r]),
+                                                      hrs, lh[j] + rowoff, 0, 0);
+            }
+        }
+        return;
       }
-      continue;
-    }
-    float* cbase;
-    uint32_t ldc;
-    if (OP == MOONEP_WGRAD) {
-      cbase = (te.wrow < g.E ? g.grad_home + int64_t(te.wrow) * wsz
-                             : g.reduce_buf + int64_t(te.wrow - g.E) * wsz) +
-              int64_t(m0) * g.Hp + n0;
-      ldc = g.Hp;
-    } else {
-      cbase = g.c + (int64_t(te.rowbase) + m0) * Ndim + n0;
-      ldc = Ndim;
-    }
-    const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
-    if constexpr (SWAP) {
-      // lane holds row wm*WM + i*16 + lane%16, columns wn*WN + j*16 + 4*(lane/16) + (0..3);
-      // a 4-column group is all in or all out (the column count is a multiple of 64)
-      const uint32_t lrow = uint32_t(wm * WM + r16) * ldc * 4;
-      uint32_t lc[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = wn * WN + j * 16 + 4 * (lane >> 4);
-        lc[j] = col < cols_valid ? lrow + uint32_t(col) * 4 : kOffNone;
+      float* cbase;
+      uint32_t ldc;
+      if (OP == MOONEP_WGRAD) {
+        cbase = (te.wrow < g.E ? g.grad_home + int64_t(te.wrow) * wsz
+                               : g.reduce_buf + int64_t(te.wrow - g.E) * wsz) +
+                int64_t(m0) * g.Hp + n0;
+        ldc = g.Hp;
+      } else {
+        cbase = g.c + (int64_t(te.rowbase) + m0) * Ndim + n0;
+        ldc = Ndim;
       }
-      // The += reads run kEpiAhead row blocks ahead of the stores. The compiler keeps
-      // buffer loads and stores in program order (it cannot tell that they never
-      // overlap), so a read written after the previous block's stores would wait for a
-      // whole memory round trip of its own: FM * FN of them in a row per tile.
-      constexpr int AHEAD = kEpiAhead < FM ? kEpiAhead : FM;
-      floatx4_t old[FM][FN];
-      auto read_old = [&](int i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          old[i][j] = __builtin_bit_cast(
-              floatx4_t,
-              __builtin_amdgcn_raw_buffer_load_b128(crs, lc[j] + uint32_t(i * 16) * ldc * 4, 0, 0));
-      };
-#pragma unroll
-      for (int i = 0; i < AHEAD; ++i) read_old(i);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, old[i][j] + acc[i][j]),
-                                                 crs, lc[j] + uint32_t(i * 16) * ldc * 4, 0, 0);
-        if (i + AHEAD < FM) read_old(i + AHEAD);
-      }
-      continue;
-    }
-    uint32_t lb[FN];
-    const uint32_t lane_row = lane_rows * ldc * 4;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = wn * WN + j * 16 + r16;
-      lb[j] = col < cols_valid ? lane_row + uint32_t(col) * 4 : kOffNone;
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t rowoff = uint32_t(i * 16 + r) * ldc * 4;
+      const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
+      if constexpr (SWAP) {
+        // lane holds row wm*WM + i*16 + lane%16, columns wn*WN + j*16 + 4*(lane/16) + (0..3);
+        // a 4-column group is all in or all out (the column count is a multiple of 64)
+        const uint32_t lrow = uint32_t(row0 + r16) * ldc * 4;
+        uint32_t lc[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const uint32_t off = lb[j] + rowoff;
-          // through a scalar: a bit cast applied to the vector element itself reads
-          // element 0 (clang, gfx950 build)
-          const float v = acc[i][j][r];
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), crs, off, 0,
-                                                STREAM_OUT ? kStreamStore : 0);
+          const int col = wn * WN + j * 16 + 4 * (lane >> 4);
+          lc[j] = col < cols_valid ? lrow + uint32_t(col) * 4 : kOffNone;
         }
+        // The += reads run kEpiAhead row blocks ahead of the stores. The compiler keeps
+        // buffer loads and stores in program order (it cannot tell that they never
+        // overlap), so a read written after the previous block's stores would wait for a
+        // whole memory round trip of its own: FM * FN of them in a row per tile.
+        constexpr int AHEAD = kEpiAhead < FM ? kEpiAhead : FM;
+        floatx4_t old[FM][FN];
+        auto read_old = [&](int i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            old[i][j] = __builtin_bit_cast(
+                floatx4_t,
+                __builtin_amdgcn_raw_buffer_load_b128(crs, lc[j] + uint32_t(i * 16) * ldc * 4, 0, 0));
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) read_old(i);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i_t, old[i][j] + acc[i][j]),
+                                                   crs, lc[j] + uint32_t(i * 16) * ldc * 4, 0, 0);
+          if (i + AHEAD < FM) read_old(i + AHEAD);
+        }
+        return;
       }
+      uint32_t lb[FN];
+      const uint32_t lane_row = lane_rows * ldc * 4;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * WN + j * 16 + r16;
+        lb[j] = col < cols_valid ? lane_row + uint32_t(col) * 4 : kOffNone;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t rowoff = uint32_t(i * 16 + r) * ldc * 4;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const uint32_t off = lb[j] + rowoff;
+            // through a scalar: a bit cast applied to the vector element itself reads
+            // element 0 (clang, gfx950 build)
+            const float v = acc[i][j][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), crs, off, 0,
+                                                  STREAM_OUT ? kStreamStore : 0);
+          }
+        }
+    };
+    // WGRAD shifts two 16-row fragments of the tile from each DMA-issuing wavefront to its
+    // DMA-free SIMD partner (112 and 144 rows), which otherwise waits at the barrier. A/B
+    // at H = 4096, H' = 1408, bit-identical: 2780-2794 -> 2706-2730 us; three fragments
+    // gained 0.6% more with twice the register spills. FWD measured 0.9% / 2.4% slower with
+    // one / two fragments moved, and DGRAD (all wavefronts issue DMAs) no change with
+    // fragments moved either way, so both keep equal halves.
+    constexpr int ASYM = WAVES_M == 2 && DW < NW && OP == MOONEP_WGRAD ? 2 : 0;
+    if constexpr (ASYM != 0) {
+      if (wm == 0) tile(std::integral_constant<int, FM - ASYM>(), 0);
+      else tile(std::integral_constant<int, FM + ASYM>(), (FM - ASYM) * 16);
+    } else {
+      tile(std::integral_constant<int, FM>(), wm * WM);
+    }
   }
 }
 
