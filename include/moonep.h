@@ -189,7 +189,8 @@ int moonep_grouped_gemm(const moonep_shape* shape, int32_t op, const void* a, co
  * moonep_grouped_gemm for callers that cannot allocate device memory or hold a
  * workspace: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc. Same arguments (without the workspace), results and errors
- * as moonep_grouped_gemm, on the same kernels. Its tile lists live in a static
+ * as moonep_grouped_gemm, on the same kernels. Its tile lists and tile-queue
+ * counters (zeroed by the call's own first kernel) live in a static
  * device array of MOONEP_NOALLOC_SCRATCH_BYTES, one per device, held until the
  * process ends; the call allocates nothing, frees nothing and needs no set-up
  * (the first call on a device resolves the array's address once).

@@ -20,8 +20,10 @@ constexpr int kMinTileM = 64;
 // Sticky error word and per-call words at the head of the workspace.
 enum FlagWord {
   kFlagError = 0, kFlagPlanValid = 1, kFlagTileCount = 2, kFlagTileCountTail = 3,
+  kFlagQueue = 16,   // 2 x kQueueWords GEMM tile-queue counters
   kFlagWords = 64
 };
+constexpr int kQueueWords = 8;   // one tile-queue counter per XCD
 
 struct WsLayout {
   size_t flags, part, counts, piece_ptr, piece_tlo, piece_base, tiles, tiles_tail, total;

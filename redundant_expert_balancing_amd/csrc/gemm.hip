@@ -83,7 +83,10 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
                                                           int max_tiles,
                                                           TileEntry* __restrict__ tails,
                                                           int32_t* __restrict__ ntails,
-                                                          int max_tails) {
+                                                          int max_tails,
+                                                          int32_t* __restrict__ qcnt) {
+  // the tile-queue counters of the GEMM launches that follow (full tiles, then tails)
+  if (qcnt && threadIdx.x < 2 * kQueueWords) qcnt[threadIdx.x] = 0;
   __shared__ int swave[2][17];
   __shared__ uint64_t skey[kSortMax];
   const int EB = E + B, total = R * EB;
@@ -350,6 +353,7 @@ struct GemmArgs {
   int H, Hp, E;
   uint16_t* act;      // SwiGLU epilogue: bf16 [rows, Hp/2]
   uint16_t* h_saved;  // SwiGLU epilogue: NULL or bf16 [rows, Hp]
+  int32_t* qcnt;      // 8 per-XCD tile-queue counters, zero at launch (NULL: static order)
 };
 
 template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false,
@@ -494,7 +498,37 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   constexpr bool NEXT_STEP0 = OP == MOONEP_WGRAD && STAGES == 2;
   int base = 0;
   bool step0_issued = false;
-  for (int64_t tau = slot; tau < total; tau += G) {
+  // Per-XCD tile queues (FWD on 256 x 256 tiles, at most 8 N-tiles): the workgroups of
+  // XCD x take its tiles of the static order, (q / P) * G + x * P + q % P for queue
+  // position q, first come first served, so the tiles in flight on an XCD stay one
+  // contiguous window however far its workgroups drift apart. Thread 0 claims the next
+  // tile during the current one. A/B, bit-identical: FWD at H = 7168, H' = 2048 -0.5%
+  // (HBM reads 52.9 -> 48.1 GB per call), at H = 4096, H' = 1408 -1.5%. Wider outputs
+  // measured slower (the fused gate/up + SwiGLU, 16 N-tiles, +3.5%; H' -> H = 7168, 28
+  // N-tiles, +0.5%), as did DGRAD (+0.8%) and the 128 x 128 tiles of small calls (+4%, a
+  // claim per short tile); they keep the static order, as do WGRAD (which prefetches its
+  // next tile's first step) and the 128 x 512 tail tiles (whose ring fills the LDS).
+  constexpr bool DYN = OP == MOONEP_FWD && !SWIGLU && BM == 256 && BN == 256;
+  const bool dyn = DYN && g.qcnt != nullptr && G % 8 == 0 && NT <= 8;
+  const int xcd = int(blockIdx.x % 8), per_xcd = G / 8;
+  __shared__ int s_claim[1];   // referenced only when DYN (otherwise not allocated)
+  auto claim = [&]() {
+    if constexpr (DYN) {
+      const int q = atomicAdd(g.qcnt + xcd, 1);
+      s_claim[0] = (q / per_xcd) * G + xcd * per_xcd + q % per_xcd;
+    }
+  };
+  auto claimed = [&]() -> int64_t {
+    if constexpr (DYN) return __builtin_amdgcn_readfirstlane(s_claim[0]);
+    else return 0;
+  };
+  int64_t tau = slot;
+  if (dyn) {
+    if (threadIdx.x == 0) claim();
+    __syncthreads();
+    tau = claimed();
+  }
+  for (; tau < total; tau = dyn ? claimed() : tau + G) {
     const Task cur = task_at(tau);
     const TileEntry te = cur.te;
     const int m0 = cur.m0, n0 = cur.n0, rows_valid = cur.rows_valid;
@@ -622,6 +656,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       // step 0 landed (the later steps of the ring may still be in flight)
       wait_steps(min(STAGES, kiters) - 1);
       __syncthreads();
+      // the next tile, read after the k-loop's barriers (at least one)
+      if (dyn && threadIdx.x == 0) claim();
 #pragma unroll
       for (int h = 0; h < HALF; ++h) load(0, h, h);
       for (int kt = 0; kt < kiters; ++kt) {
@@ -977,6 +1013,7 @@ static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntail
   if (OP != MOONEP_WGRAD && tails_apart) {
     g.tiles = tails;
     g.ntiles = ntails;
+    if (g.qcnt) g.qcnt += kQueueWords;
     launch_cfg<OP, SWIGLU, TailCfg, STREAM_OUT>(g, cus, strm);
   }
 }
@@ -994,6 +1031,7 @@ struct GemmLists {
   int32_t* ntiles;
   int32_t* ntails;
   int64_t max_tiles, max_tail;
+  int32_t* qcnt;   // 2 x kQueueWords tile-queue counters
 };
 
 // Argument checks shared by the workspace and the scratch entry points; MOONEP_OK
@@ -1034,12 +1072,13 @@ static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const v
                                           mtiled ? (small ? SmallCfg::BM : TileCfg::BM) : 0,
                                           tails_apart ? kTailRows : 0,
                                           bf16 && op == MOONEP_WGRAD, w.tiles, w.ntiles,
-                                          int(w.max_tiles), w.tails, w.ntails, int(w.max_tail));
+                                          int(w.max_tiles), w.tails, w.ntails, int(w.max_tail),
+                                          w.qcnt);
   if (launch_status()) return MOONEP_EHIP;
 
   if (bf16) {
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
-               reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E, nullptr, nullptr};
+               reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E, nullptr, nullptr, w.qcnt};
     if (op == MOONEP_FWD)
       launch_bf16<MOONEP_FWD>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
     else if (op == MOONEP_DGRAD && s.Hp <= kStreamOutMaxK)
@@ -1064,7 +1103,8 @@ static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const v
 static GemmLists ws_lists(void* ws, const WsLayout& w) {
   return GemmLists{ws_ptr<TileEntry>(ws, w.tiles), ws_ptr<TileEntry>(ws, w.tiles_tail),
                    ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount,
-                   ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail, w.max_tiles, w.max_tail};
+                   ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail, w.max_tiles, w.max_tail,
+                   ws_ptr<int32_t>(ws, w.flags) + kFlagQueue};
 }
 
 // ------------------------------------------------------------------ no-alloc scratch
@@ -1090,8 +1130,9 @@ static char* scratch_ptr() {
   return static_cast<char*>(q);
 }
 
-// Scratch layout of one call: the two list counts, then the two lists, each 256-byte
-// aligned, sized as the workspace sizes them.
+// Scratch layout of one call: the two list counts (words 0 and 1) and the tile-queue
+// counters (words kFlagQueue ..), then the two lists, each 256-byte aligned, sized as the
+// workspace sizes them.
 struct ScratchLayout {
   size_t tiles, tails, total;
 };
@@ -1135,7 +1176,7 @@ extern "C" int moonep_grouped_gemm_noalloc(const moonep_shape* shape, int32_t op
   const GemmLists lists{reinterpret_cast<TileEntry*>(base + l.tiles),
                         reinterpret_cast<TileEntry*>(base + l.tails),
                         reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base) + 1,
-                        w.max_tiles, w.max_tail};
+                        w.max_tiles, w.max_tail, reinterpret_cast<int32_t*>(base) + kFlagQueue};
   return gemm_launch(*shape, op, a, b, cu_seqlens, c, grad_home, reduce_buf, lists,
                      as_stream(stream));
 }
@@ -1158,6 +1199,7 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
   TileEntry* tails = ws_ptr<TileEntry>(ws, w.tiles_tail);
   int32_t* ntiles = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCount;
   int32_t* ntails = ws_ptr<int32_t>(ws, w.flags) + kFlagTileCountTail;
+  int32_t* qcnt = ws_ptr<int32_t>(ws, w.flags) + kFlagQueue;
   const bool bf16 = s.dtype == MOONEP_BF16;
   const int cus = device_cus();
   if (cus <= 0) return MOONEP_EHIP;
@@ -1165,12 +1207,12 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
                                           bf16 ? TileCfg::BM : 0, tails_apart ? kTailRows : 0,
                                           false, tiles, ntiles, int(w.max_tiles), tails, ntails,
-                                          int(w.max_tail));
+                                          int(w.max_tail), qcnt);
   if (launch_status()) return MOONEP_EHIP;
   if (bf16) {
     GemmArgs g{static_cast<const uint16_t*>(xp), static_cast<const uint16_t*>(w1_all), nullptr,
                nullptr, nullptr, tiles, ntiles, s.H, 2 * s.Hp, s.E,
-               static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved)};
+               static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved), qcnt};
     launch_bf16<MOONEP_FWD, true>(g, tails, ntails, tails_apart, false, cus, strm);
   } else {
     gemm_fp32_swiglu_kernel<<<dim3(64, 256), 256, 0, strm>>>(
