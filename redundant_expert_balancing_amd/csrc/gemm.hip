@@ -414,6 +414,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
 
+  // Per-XCD tile queues (FWD on 256 x 256 tiles, at most 8 N-tiles): the workgroups of
+  // XCD x take its tiles of the static order, (q / P) * G + x * P + q % P for queue
+  // position q, first come first served, so the tiles in flight on an XCD stay one
+  // contiguous window however far its workgroups drift apart. Thread 0 claims the next
+  // tile during the current one. A/B, bit-identical: FWD at H = 7168, H' = 2048 -0.5%
+  // (HBM reads 52.9 -> 48.1 GB per call), at H = 4096, H' = 1408 -1.5%. Wider outputs
+  // measured slower (the fused gate/up + SwiGLU, 16 N-tiles, +3.5%; H' -> H = 7168, 28
+  // N-tiles, +0.5%), as did DGRAD (+0.8%) and the 128 x 128 tiles of small calls (+4%, a
+  // claim per short tile); they keep the static order, as do WGRAD (which prefetches its
+  // next tile's first step) and the 128 x 512 tail tiles (whose ring fills the LDS).
+  constexpr bool DYN = OP == MOONEP_FWD && !SWIGLU && BM == 256 && BN == 256;
+  const bool dyn = DYN && g.qcnt != nullptr && G % 8 == 0 && NT <= 8;
   // the tile of task tau: its entry, first row and column, valid rows and columns,
   // and reduction length
   struct Task {
@@ -431,15 +443,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     } else {
       // blocks of kBlockE entries x kBlockN N-tiles, so that the 32 concurrent tiles of
       // an XCD reuse each weight N-tile for four M-tiles and each activation tile for
-      // eight N-tiles
-      const int64_t eb = tau / (int64_t(kBlockE) * NT);
-      const int j = int(tau % (int64_t(kBlockE) * NT));
-      const int ge = int(min(int64_t(kBlockE), nent - eb * kBlockE));
-      const int nb = j / (ge * kBlockN), jj = j % (ge * kBlockN);
-      const int wb = min(kBlockN, NT - nb * kBlockN);
-      ent = eb * kBlockE + jj / wb;
+      // eight N-tiles. With the tile queues, whose tiles in flight stay together, blocks
+      // of 8 x 4 measured 0.8% faster at H = 7168, H' = 2048 (each weight N-tile serves
+      // eight M-tiles, each activation tile is read twice).
+      const int bE = dyn ? 8 : kBlockE, bN = dyn ? 4 : kBlockN;
+      const int64_t eb = tau / (int64_t(bE) * NT);
+      const int j = int(tau % (int64_t(bE) * NT));
+      const int ge = int(min(int64_t(bE), nent - eb * bE));
+      const int nb = j / (ge * bN), jj = j % (ge * bN);
+      const int wb = min(bN, NT - nb * bN);
+      ent = eb * bE + jj / wb;
       mt = 0;
-      nt = nb * kBlockN + jj % wb;
+      nt = nb * bN + jj % wb;
     }
     Task t;
     // the entry is uniform; readfirstlane keeps it (and the buffer descriptors built
@@ -498,18 +513,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   constexpr bool NEXT_STEP0 = OP == MOONEP_WGRAD && STAGES == 2;
   int base = 0;
   bool step0_issued = false;
-  // Per-XCD tile queues (FWD on 256 x 256 tiles, at most 8 N-tiles): the workgroups of
-  // XCD x take its tiles of the static order, (q / P) * G + x * P + q % P for queue
-  // position q, first come first served, so the tiles in flight on an XCD stay one
-  // contiguous window however far its workgroups drift apart. Thread 0 claims the next
-  // tile during the current one. A/B, bit-identical: FWD at H = 7168, H' = 2048 -0.5%
-  // (HBM reads 52.9 -> 48.1 GB per call), at H = 4096, H' = 1408 -1.5%. Wider outputs
-  // measured slower (the fused gate/up + SwiGLU, 16 N-tiles, +3.5%; H' -> H = 7168, 28
-  // N-tiles, +0.5%), as did DGRAD (+0.8%) and the 128 x 128 tiles of small calls (+4%, a
-  // claim per short tile); they keep the static order, as do WGRAD (which prefetches its
-  // next tile's first step) and the 128 x 512 tail tiles (whose ring fills the LDS).
-  constexpr bool DYN = OP == MOONEP_FWD && !SWIGLU && BM == 256 && BN == 256;
-  const bool dyn = DYN && g.qcnt != nullptr && G % 8 == 0 && NT <= 8;
   const int xcd = int(blockIdx.x % 8), per_xcd = G / 8;
   __shared__ int s_claim[1];   // referenced only when DYN (otherwise not allocated)
   auto claim = [&]() {
