@@ -14,12 +14,17 @@ namespace moonep {
 constexpr int kChunkTokens = 64;
 // Chunks per partition of the planner's column scan (16 wavefronts x 4 chunks).
 constexpr int kScanPart = 64;
+// Layers of at most kFusedMaxChunks chunks count, scan and solve in one launch:
+// kFusedChunks chunks (one per wavefront) per workgroup, each workgroup a partition.
+constexpr int kFusedChunks = 16;
+constexpr int kFusedMaxChunks = 256;
 // Smallest GEMM M tile; sizes the tile list in the workspace.
 constexpr int kMinTileM = 64;
 
 // Sticky error word and per-call words at the head of the workspace.
 enum FlagWord {
   kFlagError = 0, kFlagPlanValid = 1, kFlagTileCount = 2, kFlagTileCountTail = 3,
+  kFlagPlanArrive = 4,   // workgroups of the fused planner done counting (back to 0 after)
   kFlagQueue = 16,   // 2 x kQueueWords GEMM tile-queue counters
   kFlagWords = 64
 };
@@ -27,7 +32,7 @@ constexpr int kQueueWords = 8;   // one tile-queue counter per XCD
 
 struct WsLayout {
   size_t flags, part, counts, piece_ptr, piece_tlo, piece_base, tiles, tiles_tail, total;
-  int64_t nchunk, npart, max_pieces, max_tiles, max_tail;
+  int64_t nchunk, npart, nfused, max_pieces, max_tiles, max_tail;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -38,12 +43,14 @@ inline WsLayout ws_layout(const moonep_shape& s) {
   const int64_t SK = int64_t(s.S) * s.K;
   w.nchunk = (N + kChunkTokens - 1) / kChunkTokens;
   w.npart = (w.nchunk + kScanPart - 1) / kScanPart;
+  w.nfused = w.nchunk > 0 && w.nchunk <= kFusedMaxChunks
+                 ? (w.nchunk + kFusedChunks - 1) / kFusedChunks : 0;
   w.max_pieces = int64_t(s.E) + 2 * int64_t(s.R) + 8;
   w.max_tiles = int64_t(s.R) * ((SK + kMinTileM - 1) / kMinTileM + s.E + s.B) + 1;
   w.max_tail = int64_t(s.R) * (s.E + s.B) + 1;   // at most one short tail per segment
   size_t o = 0;
   w.flags = o;      o = align256(o + kFlagWords * 4);
-  w.part = o;       o = align256(o + size_t(w.npart) * s.E * 4);
+  w.part = o;       o = align256(o + size_t(w.npart > w.nfused ? w.npart : w.nfused) * s.E * 4);
   w.counts = o;     o = align256(o + size_t(w.nchunk) * s.E * 4);
   w.piece_ptr = o;  o = align256(o + size_t(s.E + 1) * 4);
   w.piece_tlo = o;  o = align256(o + size_t(w.max_pieces) * 4);

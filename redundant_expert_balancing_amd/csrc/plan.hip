@@ -5,7 +5,9 @@
 // rank's static S*K buffer [ai-maestro.online "Moonshot AI open-sources MoonEP",
 // sections "The core idea: dynamic redundant experts" and "The memory
 // contract"]. The pages fix only the invariants; the rule implemented is stated
-// in moonep.h (moonep_plan). Four launches, no host synchronisation:
+// in moonep.h (moonep_plan). Four launches, no host synchronisation (on layers of at
+// most kFusedMaxChunks chunks, count, scan and solve share one launch: see
+// plan_count_solve_kernel):
 //
 //   count   one wavefront per chunk of 64 tokens: per-chunk expert histogram
 //           (LDS atomics) into counts[chunk][E]; flags bad or repeated ids.
@@ -42,10 +44,14 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive scan across one wavefront; *total gets the wavefront sum.
+// Sum over a wavefront whose 64 lanes are all active: lane 63 of the inclusive scan,
+// read into a scalar register (no LDS round trip).
+__device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
+
+// Exclusive scan across one wavefront (all 64 lanes active); *total gets the sum.
 __device__ inline int wave_excl_scan(int v, int* total) {
   const int incl = wave_incl_scan(v);
-  *total = __shfl(incl, 63, 64);
+  *total = __builtin_amdgcn_readlane(incl, 63);
   return incl - v;
 }
 
@@ -69,6 +75,33 @@ __device__ inline int block_excl_scan(int v, int* swave, int* total) {
 }
 
 // ---------------------------------------------------------------- count
+// One token's K expert ids into an LDS histogram; returns the error bits it finds. The
+// ids are loaded 8 at a time, all 8 loads in flight together.
+__device__ inline int count_token(const int32_t* row, int K, int E, int32_t* hist) {
+  int err = 0;
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = k0 + i < K ? row[k0 + i] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = v[i];
+      if (k0 + i >= K) break;
+      if (e < 0 || e >= E) {
+        err |= MOONEP_ERR_ID_RANGE;
+        continue;
+      }
+      for (int k2 = 0; k2 < k0; ++k2)  // ids of earlier batches (K > 8 only)
+        if (row[k2] == e) err |= MOONEP_ERR_ID_DUP;
+#pragma unroll
+      for (int j = 0; j < i; ++j)
+        if (v[j] == e) err |= MOONEP_ERR_ID_DUP;
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  return err;
+}
+
 __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restrict__ topk, int N,
                                                          int K, int E, int nchunk,
                                                          int32_t* __restrict__ counts,
@@ -79,21 +112,8 @@ __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restri
   for (int e = lane; e < E; e += 64) hist[e] = 0;
   __syncthreads();
   const int c = blockIdx.x * kWavesPerBlock + w;
-  int err = 0;
   const int g = c * kChunkTokens + lane;
-  if (c < nchunk && g < N) {
-    const int32_t* row = topk + int64_t(g) * K;
-    for (int k = 0; k < K; ++k) {
-      const int e = row[k];
-      if (e < 0 || e >= E) {
-        err |= MOONEP_ERR_ID_RANGE;
-        continue;
-      }
-      for (int k2 = 0; k2 < k; ++k2)
-        if (row[k2] == e) err |= MOONEP_ERR_ID_DUP;
-      atomicAdd(&hist[e], 1);
-    }
-  }
+  const int err = c < nchunk && g < N ? count_token(topk + int64_t(g) * K, K, E, hist) : 0;
   __syncthreads();
   if (c < nchunk)
     for (int e = lane; e < E; e += 64) counts[int64_t(c) * E + e] = hist[e];
@@ -310,8 +330,9 @@ __device__ inline void donor_tree(const SolveArgs& a, int* sm, const SolveLds& L
   }
 }
 
-__global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) {
-  extern __shared__ int sm[];
+// The solve step, run by one workgroup of kSolveThreads threads over the LDS area `sm`
+// (SolveLds(R, E, B).total ints).
+__device__ __forceinline__ void solve_plan(const SolveArgs& a, int* sm) {
   const SolveLds L(a.R, a.E, a.B);
   const int tid = threadIdx.x;
   const int EB = a.E + a.B;
@@ -336,8 +357,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
     sm[L.T + e] = run;
     sum += run;
   }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  sum = unsigned(wave_sum(int(sum)));  // below 2^31: a wavefront's share of N*K
   if ((tid & 63) == 0 && sum) atomicAdd(&s_total, sum);
   for (int i = tid; i < a.R * EB; i += kSolveThreads) sm[L.rowlen + i] = 0;
   for (int i = tid; i < a.R * a.B; i += kSolveThreads) a.replica[i] = -1;
@@ -359,9 +379,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
     for (int p = w; p < a.R; p += kSolveThreads / 64) {
       const int e = p * a.G + lane;
       const int te = lane < a.G ? sm[L.T + e] : 0;
-      int s = te;
-#pragma unroll
-      for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+      const int s = wave_sum(te);
       if (lane == 0) sm[L.L + p] = s;
       int pos = 0;
       for (int j = 0; j < a.G; ++j) {
@@ -403,7 +421,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
         const int t = s < a.G ? sm[L.T + e] : 0;
         const int incl = wave_incl_scan(t);
         if (s < a.G) sm[L.off + e] = carry + incl - t;
-        carry += __shfl(incl, 63, 64);
+        carry += __builtin_amdgcn_readlane(incl, 63);
       }
     }
   }
@@ -476,7 +494,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
           a.cu[q * (EB + 1) + i + 1] = carry + incl;
           sm[L.rowlen + q * EB + i] = carry + incl - v;
         }
-        carry += __shfl(incl, 63, 64);
+        carry += __builtin_amdgcn_readlane(incl, 63);
       }
     }
   }
@@ -502,6 +520,56 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) 
   }
 }
 
+__global__ __launch_bounds__(kSolveThreads) void plan_solve_kernel(SolveArgs a) {
+  extern __shared__ int sm[];
+  solve_plan(a, sm);
+}
+
+// ---------------------------------------------------------------- count + scan + solve
+// Small layers (at most kFusedMaxChunks chunks): one launch of kSolveThreads-thread
+// workgroups, kFusedChunks chunks each, one per wavefront. A workgroup counts its chunks,
+// writes each chunk's exclusive prefix over its own earlier chunks into counts and its
+// totals into part[blockIdx.x] (a partition of kFusedChunks chunks). The last workgroup
+// to finish (an arrival counter after a device-scope fence; no workgroup waits for
+// another) then runs the solve step on all of them.
+__global__ __launch_bounds__(kSolveThreads) void plan_count_solve_kernel(
+    const int32_t* __restrict__ topk, int N, int nchunk, int32_t* __restrict__ counts,
+    SolveArgs a) {
+  extern __shared__ int sm[];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int E = a.E;
+  int32_t* hist = sm + w * E;  // [kFusedChunks][E], then the solve step's area
+  for (int e = lane; e < E; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * kFusedChunks;
+  const int c = c0 + w;
+  const int g = c * kChunkTokens + lane;
+  const int err = c < nchunk && g < N ? count_token(topk + int64_t(g) * a.K, a.K, E, hist) : 0;
+  if (err) atomicOr(&a.flags[kFlagError], err);
+  __syncthreads();
+  for (int e = tid; e < E; e += kSolveThreads) {
+    int run = 0;
+    for (int i = 0; i < kFusedChunks; ++i) {
+      const int x = sm[i * E + e];
+      if (c0 + i < nchunk) counts[int64_t(c0 + i) * E + e] = run;
+      run += x;
+    }
+    a.part[int64_t(blockIdx.x) * E + e] = run;
+  }
+  // The barrier completes the workgroup's stores; one acquire-release counter update
+  // then publishes them device-wide and, in the last workgroup, makes every other
+  // workgroup's stores visible to the whole workgroup (it shares one L1 and L2).
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&a.flags[kFlagPlanArrive], 1, __ATOMIC_ACQ_REL,
+                                    __HIP_MEMORY_SCOPE_AGENT) == int(gridDim.x) - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) a.flags[kFlagPlanArrive] = 0;  // ready for the layer's next plan
+  solve_plan(a, sm);
+}
+
 // ---------------------------------------------------------------- assign
 // The piece table is staged in LDS by the workgroup; each wavefront loads the ids
 // of 8 steps at once, so a step waits on no global load.
@@ -509,7 +577,7 @@ constexpr int kAssignBatch = 8;
 
 __global__ __launch_bounds__(256) void plan_assign_kernel(
     const int32_t* __restrict__ topk, int N, int K, int E, int nchunk, int nbits,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ part,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ part, int part_chunks,
     const int32_t* __restrict__ piece_ptr, const int32_t* __restrict__ piece_tlo,
     const int32_t* __restrict__ piece_base, int max_pieces, const int32_t* __restrict__ flags,
     int32_t* __restrict__ slot_map, int32_t* __restrict__ src_index) {
@@ -537,7 +605,7 @@ __global__ __launch_bounds__(256) void plan_assign_kernel(
     vv[j] = u < u1 ? topk[u] : 0;
   }
   if (have) {
-    const int32_t* pp = part + int64_t(c / kScanPart) * E;
+    const int32_t* pp = part + int64_t(c / part_chunks) * E;
     for (int e = lane; e < E; e += 64) run[e] = base[int64_t(c) * E + e] + pp[e];
   }
   for (int i = threadIdx.x; i <= E; i += blockDim.x) s_ptr[i] = piece_ptr[i];
@@ -626,36 +694,44 @@ extern "C" int moonep_plan(const moonep_shape* shape, const int32_t* topk_idx, i
   int32_t* pbase = ws_ptr<int32_t>(ws, w.piece_base);
   const size_t chunk_lds = size_t(kWavesPerBlock) * s.E * 4;
   const int chunk_blocks = (nchunk + kWavesPerBlock - 1) / kWavesPerBlock;
-
-  if (nchunk > 0) {
-    plan_count_kernel<<<chunk_blocks, 256, chunk_lds, strm>>>(topk_idx, N, s.K, s.E, nchunk,
-                                                              counts, flags);
-    if (launch_status()) return MOONEP_EHIP;
-  }
-  if (nchunk > 0) {
-    plan_scan_kernel<<<dim3((s.E + 63) / 64, unsigned(w.npart)), 1024, 0, strm>>>(counts, nchunk,
-                                                                                  s.E, part);
-    if (launch_status()) return MOONEP_EHIP;
-  }
+  const size_t solve_lds = size_t(SolveLds(s.R, s.E, s.B).total) * 4;
+  if (solve_lds > 64 * 1024) return MOONEP_ELIMIT;
+  // one launch for count, scan and solve when the layer is small and the histograms of
+  // a workgroup's chunks fit the same LDS area
+  const size_t hist_lds = size_t(kFusedChunks) * s.E * 4;
+  const size_t fused_lds = hist_lds > solve_lds ? hist_lds : solve_lds;
+  const bool fused = w.nfused > 0 && fused_lds <= 60 * 1024;
 
   SolveArgs a;
   a.R = s.R; a.S = s.S; a.E = s.E; a.K = s.K; a.B = s.B; a.G = s.E / s.R; a.SK = s.S * s.K;
   a.NK = int64_t(N) * s.K;
-  a.part = part; a.npart = int(w.npart); a.cu = cu_seqlens; a.replica = replica_expert;
-  a.piece_ptr = pptr; a.piece_tlo = ptlo; a.piece_base = pbase; a.flags = flags;
-  const size_t solve_lds = size_t(SolveLds(s.R, s.E, s.B).total) * 4;
-  if (solve_lds > 64 * 1024) return MOONEP_ELIMIT;
-  plan_solve_kernel<<<1, kSolveThreads, solve_lds, strm>>>(a);
-  if (launch_status()) return MOONEP_EHIP;
+  a.part = part; a.npart = int(fused ? w.nfused : w.npart); a.cu = cu_seqlens;
+  a.replica = replica_expert; a.piece_ptr = pptr; a.piece_tlo = ptlo; a.piece_base = pbase;
+  a.flags = flags;
+  if (fused) {
+    plan_count_solve_kernel<<<unsigned(w.nfused), kSolveThreads, fused_lds, strm>>>(
+        topk_idx, N, nchunk, counts, a);
+    if (launch_status()) return MOONEP_EHIP;
+  } else {
+    if (nchunk > 0) {
+      plan_count_kernel<<<chunk_blocks, 256, chunk_lds, strm>>>(topk_idx, N, s.K, s.E, nchunk,
+                                                                counts, flags);
+      if (launch_status()) return MOONEP_EHIP;
+      plan_scan_kernel<<<dim3((s.E + 63) / 64, unsigned(w.npart)), 1024, 0, strm>>>(
+          counts, nchunk, s.E, part);
+      if (launch_status()) return MOONEP_EHIP;
+    }
+    plan_solve_kernel<<<1, kSolveThreads, solve_lds, strm>>>(a);
+    if (launch_status()) return MOONEP_EHIP;
+  }
 
   if (nchunk > 0) {
     int nbits = 0;
     while ((1 << nbits) < s.E) ++nbits;
     const size_t assign_lds = chunk_lds + (size_t(s.E) + 1 + 2 * size_t(w.max_pieces)) * 4;
     plan_assign_kernel<<<chunk_blocks, 256, assign_lds, strm>>>(
-        topk_idx, N, s.K, s.E, nchunk, nbits, counts, part, pptr, ptlo, pbase,
-        int(w.max_pieces), flags, slot_map,
-        src_index);
+        topk_idx, N, s.K, s.E, nchunk, nbits, counts, part, fused ? kFusedChunks : kScanPart,
+        pptr, ptlo, pbase, int(w.max_pieces), flags, slot_map, src_index);
     if (launch_status()) return MOONEP_EHIP;
   }
   return MOONEP_OK;

@@ -72,6 +72,13 @@ EDGE = [
     (32, 8, 128, 4, "train", None, [0]),         # many ranks
     (64, 16, 64, 2, "train", None, [0, 1]),      # 64 ranks of one expert each (B = 1)
     (8, 100, 928, 8, "infer", 95, list(range(40))),  # R*(E+B+1) = 8192, the size limit
+    # layers of at most 256 chunks of 64 tokens count, scan and solve in one launch of
+    # 16-chunk workgroups; larger ones, or ones whose 16 histograms overflow 60 KiB of
+    # LDS, take four launches
+    (8, 296, 128, 6, "infer", 3, [0, 1, 2]),     # 37 chunks: a last workgroup of 5
+    (8, 2048, 64, 4, "train", None, [0, 1, 2]),  # 256 chunks: the largest one-launch plan
+    (1, 16385, 8, 2, "train", None, [0]),        # 257 chunks: four launches
+    (8, 40, 960, 8, "infer", 0, list(range(20))),  # histograms fill the 60 KiB exactly
 ]
 
 
