@@ -96,7 +96,10 @@ int moonep_validate_shape(const moonep_shape* shape);
  */
 size_t moonep_workspace_bytes(const moonep_shape* shape);
 
-/* Zero the workspace (enqueued on `stream`). Required once before first use. */
+/* Zero the workspace (enqueued on `stream`). Required once before first use: besides
+ * the sticky error word, the workspace holds a counter that the planner of a small
+ * layer (at most 16384 tokens) counts up within a call and sets back to 0 at its end,
+ * and a later call relies on finding it at 0. */
 int moonep_workspace_init(const moonep_shape* shape, void* ws, size_t ws_bytes, void* stream);
 
 /*
