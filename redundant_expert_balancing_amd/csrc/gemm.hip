@@ -10,7 +10,9 @@
 //           128 rows; WGRAD's entries are whole segments, longest first.
 //   gemm    a persistent kernel walks entry x N-tile (x M-tile for WGRAD) with
 //           256 x 256 tiles; the 32 concurrent tiles of one XCD form a block of 4
-//           entries x 8 N-tiles, so they share operand slices in that XCD's L2.
+//           entries x 8 N-tiles, so they share operand slices in that XCD's L2 (FWD
+//           calls of at most 8 N-tiles: blocks of 8 x 4, which the workgroups of each
+//           XCD claim in order from a counter of their own).
 //   tails   (FWD, DGRAD) the same kernel with 128 x 512 tiles over the tail list:
 //           half the MFMAs a 256 x 256 tile spends on a tail of 1..128 rows.
 //
