@@ -12,8 +12,8 @@ Prints ONE JSON line (rank 0). Besides the contract fields:
   roofline      the grouped GEMM (dominant kernel) against dense bf16 MFMA peak;
                 its average duration comes from HIP events around every GEMM
                 call inside the timed region, on the stream it runs on (one call
-                = the tile-list kernel, the 256x256-tile kernel and the
-                short-tail kernel); traffic = HBM bytes of both GEMM kernels;
+                = the tile-list kernel and the 256x256-tile kernel, which also
+                runs the segment tails); traffic = HBM bytes of the GEMM kernel;
   cpu_baseline  the CPU oracle stage by stage (plan, permute, combine on one thread;
                 the float64 dense projection on every core; the training backward of
                 the training-backward layer), each on a bounded sample scaled to the
@@ -326,7 +326,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(),
-                "kernel": "moonep_grouped_gemm FWD: gemm_bf16_kernel 256x256 tiles + 128x512 tails",
+                "kernel": "moonep_grouped_gemm FWD: gemm_bf16_kernel 256x256 tiles (segment tails included)",
                 "avg_launch_ms": round(gemm_ms, 4), "flop_per_launch": flops}
 
     out = {

@@ -6,15 +6,18 @@
 //
 //   tiles   one workgroup turns cu_seqlens [R, E+B+1] into compact lists of work
 //           entries (segment start row, weight row, M offset, length): 256-row
-//           M-tiles, and (FWD, DGRAD) a second list of segment tails of at most
-//           128 rows; WGRAD's entries are whole segments, longest first.
+//           M-tiles, and (DGRAD, the fused gate/up projection) a second list of
+//           segment tails of at most 128 rows; WGRAD's entries are whole segments,
+//           longest first.
 //   gemm    a persistent kernel walks entry x N-tile (x M-tile for WGRAD) with
 //           256 x 256 tiles; the 32 concurrent tiles of one XCD form a block of 4
 //           entries x 8 N-tiles, so they share operand slices in that XCD's L2 (FWD
 //           calls of at most 8 N-tiles: blocks of 8 x 4, which the workgroups of each
 //           XCD claim in order from a counter of their own).
-//   tails   (FWD, DGRAD) the same kernel with 128 x 512 tiles over the tail list:
-//           half the MFMAs a 256 x 256 tile spends on a tail of 1..128 rows.
+//   tails   (DGRAD, fused gate/up) the same kernel with 128 x 512 tiles over the
+//           tail list: half the MFMAs a 256 x 256 tile spends on a tail of 1..128
+//           rows. A plain FWD keeps its tails in the 256 x 256 launch, where the
+//           wavefronts of the tile's empty row group sit them out.
 //
 // bf16 path: v_mfma_f32_16x16x32_bf16 with float32 accumulation (a 128 x 64
 // wavefront tile as 8 x 4 blocks: per flop, half the accumulator register traffic
@@ -542,11 +545,50 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     const bool has_next = NEXT_STEP0 && tau + G < total;
     auto stage = [&](int kt) { return uint32_t((base + kt) & (STAGES - 1)) * STAGE; };
     auto issue = [&](int kt) { issue_task(cur, kt, lds0 + stage(kt)); };
+    // wait until at most n later steps of this wavefront's DMAs are in flight
+    auto wait_steps = [&](int n) {
+      if (wid >= DW) return;   // no DMAs of its own
+      if constexpr (STAGES > 3) {
+        if (n >= 3) { wait_vm<3 * DMA_PER_STEP>(); return; }
+      }
+      if constexpr (STAGES > 2) {
+        if (n == 2) { wait_vm<2 * DMA_PER_STEP>(); return; }
+      }
+      if (n == 1) wait_vm<DMA_PER_STEP>();
+      else wait_vm<0>();
+    };
 
     // the tile's MFMAs, ring and epilogue for a wavefront of FM 16-row fragments whose
     // rows start at row0 of the tile
     auto tile = [&](auto fm_c, int row0) {
       constexpr int FM = decltype(fm_c)::value;
+      // A tile whose valid rows all lie in the first row group (a segment's last tile)
+      // leaves the second group's wavefronts without a row: they skip the MFMAs, LDS
+      // reads and stores, issue their share of the DMAs and meet every barrier, so their
+      // SIMD partners run alone for about half the tile's time. This is what a plain FWD
+      // does with its segment tails of at most 128 rows: run there, next to the same
+      // segment's full tiles, each tail finds the weight slice in L2, where the tail
+      // launch re-read it from HBM. A/B, bit-identical: FWD at H = 7168, H' = 2048 -0.3
+      // to -0.4%, at H = 4096, H' = 1536 -2.2%, at H = 4096, H' = 1408 -3.2%, the FFN down
+      // projection (H' -> H = 7168) -2.3%. DGRAD (+1%) and the fused gate/up projection
+      // (+6% at one of four imbalance points) measured slower and keep the tail launch.
+      if constexpr (OP != MOONEP_WGRAD && WAVES_M == 2) {
+        if (row0 >= rows_valid) {   // uniform per wavefront
+          __syncthreads();
+          if (!step0_issued) issue(0);
+#pragma unroll
+          for (int k = 1; k < STAGES; ++k)
+            if (k < kiters) issue(k);
+          wait_steps(min(STAGES, kiters) - 1);
+          __syncthreads();
+          for (int kt = 0; kt < kiters; ++kt) {
+            if (kt + 1 < kiters) wait_steps(min(kt + STAGES - 1, kiters - 1) - (kt + 1));
+            __syncthreads();
+            if (kt + STAGES < kiters) issue(kt + STAGES);
+          }
+          return;
+        }
+      }
       floatx4_t acc[FM][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -561,18 +603,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 #pragma unroll
       for (int k = 1; k < STAGES; ++k)
         if (k < kiters) issue(k);
-      // wait until at most n later steps of this wavefront's DMAs are in flight
-      auto wait_steps = [&](int n) {
-        if (wid >= DW) return;   // no DMAs of its own
-        if constexpr (STAGES > 3) {
-          if (n >= 3) { wait_vm<3 * DMA_PER_STEP>(); return; }
-        }
-        if constexpr (STAGES > 2) {
-          if (n == 2) { wait_vm<2 * DMA_PER_STEP>(); return; }
-        }
-        if (n == 1) wait_vm<DMA_PER_STEP>();
-        else wait_vm<0>();
-      };
 
       // The fragments of half a step (one 32-deep substep: FM + FN operands of 4
       // registers) live in registers: a whole step's would need 96 registers beside
@@ -960,7 +990,7 @@ static int device_cus() {
 struct TileCfg {
   static constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, STAGES = 2;
 };
-// Segment tails of at most kTailRows rows (FWD, DGRAD): 128 x 512 tiles, the same
+// Segment tails of at most kTailRows rows (DGRAD, fused gate/up): 128 x 512 tiles, the same
 // 128 x 64 wavefront tile with the 8 wavefronts side by side in N, a 160 KiB
 // 2-stage ring (16 KiB + 64 KiB per stage).
 // A 256 x 256 tile spends as many MFMAs on a tail of 1..128 rows as on a full one;
@@ -988,7 +1018,8 @@ static bool small_tiles(const moonep_shape& s, int ncols, int cus) {
   return full_tiles(s, ncols) < 2 * int64_t(cus);
 }
 
-// Whether segment tails get their own launch. The split halves the MFMAs spent on
+// Whether segment tails get their own launch (DGRAD and the fused gate/up projection;
+// a plain FWD runs them in its 256 x 256 launch). The split halves the MFMAs spent on
 // tails, but the tail launch waits for the full-tile launch; a GEMM of under four
 // rounds of full tiles is latency-bound, and there the second launch costs more than
 // it saves (a layer of 32768 slots, H = 1024, H' = 512: 137 -> 101 us without it).
@@ -1072,7 +1103,7 @@ static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const v
   if (cus <= 0) return MOONEP_EHIP;
   const int ncols = op == MOONEP_DGRAD ? s.H : s.Hp;
   const bool small = mtiled && small_tiles(s, ncols, cus);
-  const bool tails_apart = mtiled && split_tails(s, ncols, cus);
+  const bool tails_apart = op == MOONEP_DGRAD && mtiled && split_tails(s, ncols, cus);
   gemm_tiles_kernel<<<1, 1024, 0, strm>>>(cu_seqlens, s.R, s.E, s.B, s.S * s.K,
                                           mtiled ? (small ? SmallCfg::BM : TileCfg::BM) : 0,
                                           tails_apart ? kTailRows : 0,

@@ -1,12 +1,13 @@
 """GPU parity where the other modules sample: the short-tail GEMM launch compared in
 full, and whole output buffers at the full layer sizes.
 
-* Layers large enough that the grouped GEMM gives segment tails (at most 128 rows)
-  a launch of their own, but with a small hidden size, so the oracle computes every
-  output: forward and backward of one projection and of the full expert FFN,
-  element by element. The split is asserted (the GEMM takes it when a call has at
-  least four rounds of full 256-row tiles over the compute units) and so are the
-  tails themselves.
+* Layers large enough that the grouped GEMM treats segment tails (at most 128 rows)
+  apart, but with a small hidden size, so the oracle computes every output: forward
+  and backward of one projection and of the full expert FFN, element by element.
+  DGRAD and the fused gate/up projection give the tails a launch of their own; a
+  plain forward runs them in its 256-row tiles with the empty row group's
+  wavefronts idle. The size (at least four rounds of full 256-row tiles over the
+  compute units) is asserted, and so are the tails themselves.
 * Full-size layers, outputs poisoned with NaN before the call: every element of
   every output buffer is finite afterwards, and the first and last slot of every
   non-empty segment, plus the first slot of the segment's last 256-row tile (a tail
@@ -43,8 +44,9 @@ def _host(t):
 
 
 def _tails_split(cfg, ncols) -> bool:
-    """Whether the GEMM over R*S*K rows and `ncols` output columns splits its tails off:
-    at least four rounds of full 256 x 256 tiles over the device's compute units."""
+    """Whether the GEMM over R*S*K rows and `ncols` output columns is large enough to
+    treat its tails apart (DGRAD and the fused gate/up projection launch them on their
+    own): at least four rounds of full 256 x 256 tiles over the device's compute units."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     return cfg.R * cfg.S * cfg.K // TILE_M * -(-ncols // TILE_M) >= 4 * cus
 
