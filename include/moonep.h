@@ -175,8 +175,10 @@ int moonep_dispatch(const moonep_shape* shape, int32_t width, const void* src,
  *          i <  E: grad_home[i]         += D   (grad_home float32 [E, H, Hp])
  *          i >= E: reduce_buf[q][i - E] += D   (reduce_buf float32 [R, B, H, Hp])
  *          [maestro "The memory contract": fp32 grads mirror the weight layout,
- *          rows [E,E+B) backed by a separate reduce buffer]. In training each
- *          grad_home row is written by its home rank only, so there is no race.
+ *          rows [E,E+B) backed by a separate reduce buffer]. WGRAD requires rank
+ *          q's rows i < E to be empty unless i is one of q's home experts, as a
+ *          training plan leaves them: each grad_home row then has one writer (two
+ *          ranks adding into one row would race).
  * Inputs bf16 with float32 accumulation (MFMA), or float32 throughout.
  * Requires H and Hp multiples of 64. DGRAD and WGRAD on an inference layer
  * return MOONEP_EMODE.
