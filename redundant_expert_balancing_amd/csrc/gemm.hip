@@ -362,7 +362,7 @@ struct GemmArgs {
 };
 
 template <int OP, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU = false,
-          bool STREAM_OUT = false, int STAGES = 2>
+          bool STREAM_OUT = false, int STAGES = 2, bool HALFN = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -559,9 +559,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     };
 
     // the tile's MFMAs, ring and epilogue for a wavefront of FM 16-row fragments whose
-    // rows start at row0 of the tile
-    auto tile = [&](auto fm_c, int row0) {
+    // rows start at row0 and whose WN columns start at col0 of the tile; an idle
+    // wavefront (HALFN) only keeps the ring's DMAs and barriers
+    auto tile = [&](auto fm_c, int row0, int col0_arg, bool idle) {
       constexpr int FM = decltype(fm_c)::value;
+      const int col0 = HALFN ? col0_arg : wn * WN;
       // A tile whose valid rows all lie in the first row group (a segment's last tile)
       // leaves the second group's wavefronts without a row: they skip the MFMAs, LDS
       // reads and stores, issue their share of the DMAs and meet every barrier, so their
@@ -572,8 +574,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       // to -0.4%, at H = 4096, H' = 1536 -2.2%, at H = 4096, H' = 1408 -3.2%, the FFN down
       // projection (H' -> H = 7168) -2.3%. DGRAD (+1%) and the fused gate/up projection
       // (+6% at one of four imbalance points) measured slower and keep the tail launch.
-      if constexpr (OP != MOONEP_WGRAD && WAVES_M == 2) {
-        if (row0 >= rows_valid) {   // uniform per wavefront
+      if constexpr (HALFN || (OP != MOONEP_WGRAD && WAVES_M == 2)) {
+        if ((HALFN && idle) ||
+            (OP != MOONEP_WGRAD && WAVES_M == 2 && row0 >= rows_valid)) {   // uniform
           __syncthreads();
           if (!step0_issued) issue(0);
 #pragma unroll
@@ -582,9 +585,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
           wait_steps(min(STAGES, kiters) - 1);
           __syncthreads();
           for (int kt = 0; kt < kiters; ++kt) {
-            if (kt + 1 < kiters) wait_steps(min(kt + STAGES - 1, kiters - 1) - (kt + 1));
+            const bool more = kt + 1 < kiters;
+            if (more) wait_steps(min(kt + STAGES - 1, kiters - 1) - (kt + 1));
             __syncthreads();
             if (kt + STAGES < kiters) issue(kt + STAGES);
+            else if (!more && has_next) issue_task(task_at(tau + G), 0, lds0 + stage(kt));
+          }
+          if constexpr (NEXT_STEP0) {
+            step0_issued = has_next;
+            base = (base + kiters - 1) & 1;
           }
           return;
         }
@@ -623,7 +632,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[buf][i] = OA::frag(st, row0 + i * 16, ks, lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, wn * WN + j * 16, ks, lane);
+        for (int j = 0; j < FN; ++j) fb[buf][j] = OB::frag(st + OA::BYTES, col0 + j * 16, ks, lane);
       };
       auto mfma = [&](int buf, int i, int j) {
         if constexpr (SWAP)
@@ -730,7 +739,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       if constexpr (SWIGLU) {
         // in each 64-column group jp of the wavefront, blocks 4jp, 4jp+1 hold the gate
         // and blocks 4jp+2, 4jp+3 the up value of intermediate columns
-        // n0/2 + wn*WN/2 + jp*32 + (0..31); a partial tile ends on a 64-column boundary,
+        // n0/2 + col0/2 + jp*32 + (0..31); a partial tile ends on a 64-column boundary,
         // so each group is all in or all out
         const int hact = g.Hp / 2;
         const int64_t row0 = int64_t(te.rowbase) + m0;
@@ -740,8 +749,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
         uint32_t la[FN / 4];
 #pragma unroll
         for (int jp = 0; jp < FN / 4; ++jp)
-          la[jp] = wn * WN + jp * 64 < cols_valid
-                       ? arow + uint32_t(wn * (WN / 2) + jp * kSwigluBlock + r16) * 2
+          la[jp] = col0 + jp * 64 < cols_valid
+                       ? arow + uint32_t(col0 / 2 + jp * kSwigluBlock + r16) * 2
                        : kOffNone;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -764,7 +773,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
           uint32_t lh[FN];
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            lh[j] = wn * WN + (j / 4) * 64 < cols_valid ? hrow + uint32_t(wn * WN + j * 16 + r16) * 2
+            lh[j] = col0 + (j / 4) * 64 < cols_valid ? hrow + uint32_t(col0 + j * 16 + r16) * 2
                                                         : kOffNone;
 #pragma unroll
           for (int i = 0; i < FM; ++i)
@@ -792,13 +801,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       }
       const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, clamp_bytes(int64_t(rows_valid) * ldc * 4));
       if constexpr (SWAP) {
-        // lane holds row wm*WM + i*16 + lane%16, columns wn*WN + j*16 + 4*(lane/16) + (0..3);
+        // lane holds row row0 + i*16 + lane%16, columns col0 + j*16 + 4*(lane/16) + (0..3);
         // a 4-column group is all in or all out (the column count is a multiple of 64)
         const uint32_t lrow = uint32_t(row0 + r16) * ldc * 4;
         uint32_t lc[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = wn * WN + j * 16 + 4 * (lane >> 4);
+          const int col = col0 + j * 16 + 4 * (lane >> 4);
           lc[j] = col < cols_valid ? lrow + uint32_t(col) * 4 : kOffNone;
         }
         // The += reads run kEpiAhead row blocks ahead of the stores. The compiler keeps
@@ -830,7 +839,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
       const uint32_t lane_row = lane_rows * ldc * 4;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = wn * WN + j * 16 + r16;
+        const int col = col0 + j * 16 + r16;
         lb[j] = col < cols_valid ? lane_row + uint32_t(col) * 4 : kOffNone;
       }
 #pragma unroll
@@ -856,11 +865,29 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     // one / two fragments moved, and DGRAD (all wavefronts issue DMAs) no change with
     // fragments moved either way, so both keep equal halves.
     constexpr int ASYM = WAVES_M == 2 && DW < NW && OP == MOONEP_WGRAD ? 2 : 0;
+    // HALFN (calls whose last N-tile is at most half full, such as H' = 1408: 128 of 256
+    // columns): on such a tile the wavefronts of the empty half would spend every MFMA on
+    // columns that are never stored, and they share SIMDs with each other. Instead the
+    // first NW/2 wavefronts (one per SIMD) take the wave tiles of the valid half and the
+    // others only keep the ring and the barriers. A separate instance, so that the
+    // kernel of every other call keeps its code and registers. A/B, bit-identical: FWD at
+    // H = 4096, H' = 1408 -1.6%. Compiled into the shared instance instead it made the
+    // FWD at H' = 2048 (no such tiles) 1.5% slower; WGRAD on its own instance was 12%
+    // slower (one wavefront per SIMD cannot cover its transposed LDS reads).
+    int wm_t = wm, wn_t = wn;
+    bool idle = false;
+    if constexpr (HALFN && WAVES_N % 2 == 0) {
+      if (cols_valid <= BN / 2) {
+        idle = wid >= NW / 2;
+        wm_t = (wid % (NW / 2)) / (WAVES_N / 2);
+        wn_t = wid % (WAVES_N / 2);
+      }
+    }
     if constexpr (ASYM != 0) {
-      if (wm == 0) tile(std::integral_constant<int, FM - ASYM>(), 0);
-      else tile(std::integral_constant<int, FM + ASYM>(), (FM - ASYM) * 16);
+      if (wm_t == 0) tile(std::integral_constant<int, FM - ASYM>(), 0, wn_t * WN, idle);
+      else tile(std::integral_constant<int, FM + ASYM>(), (FM - ASYM) * 16, wn_t * WN, idle);
     } else {
-      tile(std::integral_constant<int, FM>(), wm * WM);
+      tile(std::integral_constant<int, FM>(), wm_t * WM, wn_t * WN, idle);
     }
   }
 }
@@ -1028,24 +1055,33 @@ static bool split_tails(const moonep_shape& s, int ncols, int cus) {
   return full_tiles(s, ncols) >= 4 * int64_t(cus);
 }
 
-template <int OP, bool SWIGLU, typename C, bool STREAM_OUT = false>
+template <int OP, bool SWIGLU, typename C, bool STREAM_OUT = false, bool HALFN = false>
 static void launch_cfg(const GemmArgs& g, int cus, hipStream_t strm) {
-  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU, STREAM_OUT, C::STAGES>
-      <<<cus, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
+  gemm_bf16_kernel<OP, C::BM, C::BN, C::WAVES_M, C::WAVES_N, SWIGLU, STREAM_OUT, C::STAGES,
+                   HALFN><<<cus, C::WAVES_M * C::WAVES_N * 64, 0, strm>>>(g);
 }
 
 // The full-tile list (on the small-tile kernel for a small call), then (FWD and DGRAD,
 // when the tails are split off) the tail list on the tail kernel.
+// Ops whose 256 x 256 launch takes the HALFN instance when the last N-tile of the call
+// is at most half full (plain FWD; WGRAD measured slower with it).
+template <int OP, bool SWIGLU>
+constexpr bool kHalfnOp = OP == MOONEP_FWD && !SWIGLU;
+
 template <int OP, bool SWIGLU = false, bool STREAM_OUT = false>
 static void launch_bf16(GemmArgs g, const TileEntry* tails, const int32_t* ntails,
-                        bool tails_apart, bool small, int cus, hipStream_t strm) {
+                        bool tails_apart, bool small, int ncols, int cus, hipStream_t strm) {
   if constexpr (OP != MOONEP_WGRAD && !SWIGLU) {
     if (small) {
       launch_cfg<OP, SWIGLU, SmallCfg, STREAM_OUT>(g, cus, strm);
       return;
     }
   }
-  launch_cfg<OP, SWIGLU, TileCfg, STREAM_OUT>(g, cus, strm);
+  const int last = ncols % TileCfg::BN;   // columns of the call's last N-tile (0: full)
+  if (kHalfnOp<OP, SWIGLU> && last > 0 && last <= TileCfg::BN / 2)
+    launch_cfg<OP, SWIGLU, TileCfg, STREAM_OUT, kHalfnOp<OP, SWIGLU>>(g, cus, strm);
+  else
+    launch_cfg<OP, SWIGLU, TileCfg, STREAM_OUT>(g, cus, strm);
   if (OP != MOONEP_WGRAD && tails_apart) {
     g.tiles = tails;
     g.ntiles = ntails;
@@ -1116,12 +1152,13 @@ static int gemm_launch(const moonep_shape& s, int32_t op, const void* a, const v
     GemmArgs g{static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), c, grad_home,
                reduce_buf, w.tiles, w.ntiles, s.H, s.Hp, s.E, nullptr, nullptr, w.qcnt};
     if (op == MOONEP_FWD)
-      launch_bf16<MOONEP_FWD>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
+      launch_bf16<MOONEP_FWD>(g, w.tails, w.ntails, tails_apart, small, ncols, cus, strm);
     else if (op == MOONEP_DGRAD && s.Hp <= kStreamOutMaxK)
-      launch_bf16<MOONEP_DGRAD, false, true>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
+      launch_bf16<MOONEP_DGRAD, false, true>(g, w.tails, w.ntails, tails_apart, small, ncols,
+                                             cus, strm);
     else if (op == MOONEP_DGRAD)
-      launch_bf16<MOONEP_DGRAD>(g, w.tails, w.ntails, tails_apart, small, cus, strm);
-    else launch_bf16<MOONEP_WGRAD>(g, w.tails, w.ntails, false, false, cus, strm);
+      launch_bf16<MOONEP_DGRAD>(g, w.tails, w.ntails, tails_apart, small, ncols, cus, strm);
+    else launch_bf16<MOONEP_WGRAD>(g, w.tails, w.ntails, false, false, ncols, cus, strm);
   } else {
     const dim3 grid(64, 256);
     const float* af = static_cast<const float*>(a);
@@ -1249,7 +1286,7 @@ extern "C" int moonep_grouped_gemm_swiglu(const moonep_shape* shape, const void*
     GemmArgs g{static_cast<const uint16_t*>(xp), static_cast<const uint16_t*>(w1_all), nullptr,
                nullptr, nullptr, tiles, ntiles, s.H, 2 * s.Hp, s.E,
                static_cast<uint16_t*>(act), static_cast<uint16_t*>(h_saved), qcnt};
-    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, tails_apart, false, cus, strm);
+    launch_bf16<MOONEP_FWD, true>(g, tails, ntails, tails_apart, false, 2 * s.Hp, cus, strm);
   } else {
     gemm_fp32_swiglu_kernel<<<dim3(64, 256), 256, 0, strm>>>(
         static_cast<const float*>(xp), static_cast<const float*>(w1_all),
