@@ -395,7 +395,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
   using OB = typename std::conditional<OP == MOONEP_DGRAD, OpK<BN, DW>, OpMN<BN, DW>>::type;
   constexpr int DMA_PER_STEP = OA::PER_WAVE + OB::PER_WAVE;   // per issuing wavefront
   constexpr int STAGE = OA::BYTES + OB::BYTES;
-  static_assert(STAGES >= 2 && (STAGES & (STAGES - 1)) == 0, "LDS ring depth: a power of two");
+  static_assert(STAGES >= 2, "LDS ring depth");
   __shared__ __align__(1024) char smem[STAGES * STAGE];
 
   const int Ndim = OP == MOONEP_DGRAD ? g.H : g.Hp;   // columns of C
@@ -543,7 +543,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
     const int cols_valid = cur.cols_valid, kdim = cur.kdim;
     const int kiters = (kdim + kBK - 1) / kBK;
     const bool has_next = NEXT_STEP0 && tau + G < total;
-    auto stage = [&](int kt) { return uint32_t((base + kt) & (STAGES - 1)) * STAGE; };
+    auto stage = [&](int kt) {
+      if constexpr ((STAGES & (STAGES - 1)) == 0) return uint32_t((base + kt) & (STAGES - 1)) * STAGE;
+      else return uint32_t(unsigned(base + kt) % STAGES) * STAGE;
+    };
     auto issue = [&](int kt) { issue_task(cur, kt, lds0 + stage(kt)); };
     // wait until at most n later steps of this wavefront's DMAs are in flight
     auto wait_steps = [&](int n) {
@@ -1029,12 +1032,15 @@ constexpr int kTailRows = TailCfg::BM;
 // Small calls (FWD and DGRAD with under two rounds of full 256 x 256 tiles over the CUs;
 // the fused SwiGLU epilogue needs 64-column wavefront tiles and keeps the large ones):
 // most of their operand lines come from HBM, not from another workgroup's L2 fetch, and
-// one 64-deep step of lookahead leaves each step waiting for HBM. 128 x 128 tiles (8
-// wavefronts of 64 x 32) in a 4-stage ring of the same 128 KiB keep three steps in
-// flight and give the CUs four times as many tiles to balance. Every output element
-// gets the same MFMAs in the same k order as with the large tiles.
+// one 64-deep step of lookahead leaves each step waiting for HBM. 256 x 128 tiles (8
+// wavefronts of 128 x 32) in a 3-stage ring of 48 KiB steps (144 KiB) keep two steps in
+// flight and give the CUs twice as many tiles to balance. Against 128 x 128 tiles in a
+// 4-stage ring (three steps of 32 KiB in flight), they read a quarter fewer LDS and DMA
+// bytes per flop: 88-91 -> 83-86 us at 32768 slots, H = 1024, H' = 512 (A/B, caches
+// flushed; 128 x 256 in 3 stages gave nothing). Every output element gets the same MFMAs
+// in the same k order as with the large tiles.
 struct SmallCfg {
-  static constexpr int BM = 128, BN = 128, WAVES_M = 2, WAVES_N = 4, STAGES = 4;
+  static constexpr int BM = 256, BN = 128, WAVES_M = 2, WAVES_N = 4, STAGES = 3;
 };
 
 static int64_t full_tiles(const moonep_shape& s, int ncols) {
