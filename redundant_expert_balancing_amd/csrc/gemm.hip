@@ -193,12 +193,13 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
     }
   }
   // A segment's last tile of at most bm/2 rows takes about half a tile's time (its second
-  // row group idles), so the workgroup that runs it claims its next tile early and runs
-  // out of phase with the rest of its XCD, whose tiles share operand lines in L2 only
-  // while they stay within a step or two of each other. Listing such entries last in each
-  // run of `group` entries (one tile-order block) lets them start last and end with the
-  // others. A/B, bit-identical: FWD at H = 7168, H' = 2048 -0.9 to -1.7% at four
-  // imbalance points; within noise at H' = 1536 and 1408.
+  // row group idles). The workgroups of an XCD claim its tiles first come first served,
+  // and its tiles share operand lines in L2 only while they stay within a step or two of
+  // each other. Listing such entries last in each run of `group` entries (one tile-order
+  // block, one round of the XCD's queue) hands the short tiles to the workgroups that
+  // finished the previous round last, so the XCD's workgroups converge instead of drifting
+  // apart. A/B, bit-identical: FWD at H = 7168, H' = 2048 -0.9 to -2.2% at four imbalance
+  // points, its fetch 63.4 -> 53.8 GB per call; within noise at H' = 1536 and 1408.
   if (group > 0 && group <= 8) {
     __syncthreads();   // the list is written
     const int listed = min(count, max_tiles);
