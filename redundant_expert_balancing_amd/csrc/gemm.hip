@@ -194,7 +194,7 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
   }
   // A segment's last tile of at most bm/2 rows takes about half a tile's time (its second
   // row group idles). The workgroups of an XCD claim its tiles first come first served,
-  // and its tiles share operand lines in L2 only while they stay within a step or two of
+  // and its tiles share operand lines in L2 only while they stay within a few steps of
   // each other. Listing such entries last in each run of `group` entries (one tile-order
   // block, one round of the XCD's queue) hands the short tiles to the workgroups that
   // finished the previous round last, so the XCD's workgroups converge instead of drifting
