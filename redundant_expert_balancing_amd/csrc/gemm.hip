@@ -73,6 +73,10 @@ __device__ inline int wave_scan_incl(int v) {
 // E + R*B = 2E <= 2048 non-empty segments, so every planned WGRAD is sorted; larger
 // counts (cu_seqlens from elsewhere, up to R*(E+B) <= 8192 rows) keep plan order.
 constexpr int kSortMax = 4096;
+// Entries of a list that the tile-list kernel builds in LDS (64 KiB); longer lists are
+// built in place in memory.
+constexpr int kStageMax = 4096;
+static_assert(kSortMax * sizeof(uint64_t) <= kStageMax * 16, "sort keys share the LDS list buffer");
 
 // M-tiles of bm rows per segment (bm = 0: one entry per whole segment). With
 // tail > 0 a segment's last M-tile goes to a second list when it has at most
@@ -95,7 +99,10 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
   // the tile-queue counters of the GEMM launches that follow (full tiles, then tails)
   if (qcnt && threadIdx.x < 2 * kQueueWords) qcnt[threadIdx.x] = 0;
   __shared__ int swave[2][17];
-  __shared__ uint64_t skey[kSortMax];
+  // sort keys (WGRAD) or the staged list (every other call): one buffer, two uses
+  __shared__ __align__(16) char s_buf[kStageMax * sizeof(TileEntry)];
+  uint64_t* skey = reinterpret_cast<uint64_t*>(s_buf);
+  TileEntry* s_ent = reinterpret_cast<TileEntry*>(s_buf);
   const int EB = E + B, total = R * EB;
   const int per = (total + 1023) / 1024;
   const int i0 = threadIdx.x * per, i1 = min(total, i0 + per);
@@ -174,6 +181,13 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
     }
     return;
   }
+  // A list that fits is built in LDS, reordered there and copied out in one coalesced
+  // pass, instead of being written to memory and read back: at 524288 slots, H = 7168,
+  // H' = 2048 (about 2250 entries) the kernel's chain of memory round trips took 24-33 us,
+  // against 12-17 us this way.
+  const int listed = min(count, max_tiles);
+  const bool staged = listed <= kStageMax;   // uniform
+  TileEntry* out = staged ? s_ent : tiles;
   for (int idx = i0; idx < i1; ++idx) {
     const int q = idx / EB, i = idx % EB;
     const int c0 = cu[q * (EB + 1) + i];
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
     split(n, f, t);
     const int step = bm > 0 ? bm : n;
     for (int j = 0; j < f; ++j) {
-      if (k < max_tiles) tiles[k] = TileEntry{q * SK + c0, wrow, j * step, n};
+      if (k < listed) out[k] = TileEntry{q * SK + c0, wrow, j * step, n};
       ++k;
     }
     if (t) {
@@ -202,17 +216,25 @@ __global__ __launch_bounds__(1024) void gemm_tiles_kernel(const int32_t* __restr
   // points, its fetch 63.4 -> 53.8 GB per call; within noise at H' = 1536 and 1408.
   if (group > 0 && group <= 8) {
     __syncthreads();   // the list is written
-    const int listed = min(count, max_tiles);
     for (int base = threadIdx.x * group; base < listed; base += 1024 * group) {
+      // unrolled, so that e[] stays in registers
       TileEntry e[8];
       const int m = min(group, listed - base);
-      for (int i = 0; i < m; ++i) e[i] = tiles[base + i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < m) e[i] = out[base + i];
       int o = base;
-      for (int i = 0; i < m; ++i)
-        if (e[i].n - e[i].m0 > bm / 2) tiles[o++] = e[i];
-      for (int i = 0; i < m; ++i)
-        if (e[i].n - e[i].m0 <= bm / 2) tiles[o++] = e[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < m && e[i].n - e[i].m0 > bm / 2) out[o++] = e[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < m && e[i].n - e[i].m0 <= bm / 2) out[o++] = e[i];
     }
+  }
+  if (staged) {
+    __syncthreads();   // the list is complete in LDS
+    for (int j = threadIdx.x; j < listed; j += 1024) tiles[j] = s_ent[j];
   }
 }
 
