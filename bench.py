@@ -59,6 +59,11 @@ def parse():
     ap.add_argument("--stack", type=int, default=0,
                     help="only time N layers at the bench shape whose prefetch slots share one "
                          "pool, prefetch serial vs on a side stream overlapped with dispatch")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor library's dense GEMM of the bench shape's size "
+                         "(hipBLASLt through torch.mm: bf16 output, and float32 output as the "
+                         "grouped GEMM writes) next to the grouped GEMM, same process and box; "
+                         "a reference for the kernel, not part of the path")
     ap.add_argument("--ffn", action="store_true",
                     help="only print per-stage microseconds of the full expert FFN (gate/up "
                          "with SwiGLU, down) forward at the bench shape and backward at the "
@@ -266,6 +271,9 @@ def main():
         return
     if args.ffn:
         ffn_table(args.stage_reps)
+        return
+    if args.vendor_gemm:
+        vendor_gemm(args.stage_reps)
         return
     if args.stack:
         stack_bench(args.stack, args.steps, args.warmup)
@@ -661,6 +669,52 @@ def stack_bench(n_layers, steps, warmup):
         stack.close()
         del stack, d, ins
         torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
+def vendor_gemm(reps):
+    """The grouped GEMM of the bench shape against the vendor library's dense GEMM
+    of the same size, M = R*S*K slots by K = H by N = H' with one weight matrix
+    (hipBLASLt through torch.mm, bf16 inputs, bf16 and float32 outputs), timed the
+    same way in one process (caches flushed before every repetition). Measurement
+    only: nothing on the path calls the vendor library."""
+    import torch
+
+    from redundant_expert_balancing_amd.layer import MoEProjection
+    from redundant_expert_balancing_amd.synth import CONFIGS, make_dense, make_routing
+
+    timed = _timer(reps)
+    cfg = CONFIGS["bench_shape"]
+    M, K, N = cfg.N * cfg.K, cfg.H, cfg.Hp
+    flop = 2.0 * M * K * N
+
+    def rate(us):
+        tf = flop / (us * 1e-6) / 1e12
+        return {"us": us, "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    out = {"shape": {"M": M, "K": K, "N": N}, "flop": flop}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((K, N), generator=g, device="cuda", dtype=torch.float32) / K ** 0.5).to(torch.bfloat16)
+    c16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    out["hipblaslt_bf16_out"] = rate(timed(lambda: torch.mm(a, w, out=c16)))
+    print(f"[vendor] bf16 out: {out['hipblaslt_bf16_out']}", file=sys.stderr, flush=True)
+    del c16
+    c32 = torch.mm(a, w, out_dtype=torch.float32)
+    out["hipblaslt_fp32_out"] = rate(timed(lambda: torch.mm(a, w, out_dtype=torch.float32)))
+    print(f"[vendor] fp32 out: {out['hipblaslt_fp32_out']}", file=sys.stderr, flush=True)
+    del a, w, c32
+    torch.cuda.empty_cache()
+
+    d = make_dense(cfg, "cuda", 0, which=("x", "W"), w_rows=cfg.E + cfg.R * cfg.B)
+    layer = MoEProjection(cfg, "cuda", w_all=d["W"])
+    for target in cfg.maxvio:
+        r = make_routing(cfg, target)
+        topk = torch.from_numpy(r.topk_idx).cuda()
+        layer.forward(topk, d["x"], torch.from_numpy(r.gates).cuda())
+        out[f"grouped maxvio={r.maxvio:.3g}"] = rate(timed(layer.gemm_fwd))
+        print(f"[vendor] grouped {target}: {out[f'grouped maxvio={r.maxvio:.3g}']}", file=sys.stderr,
+              flush=True)
     print(json.dumps(out), flush=True)
 
 
