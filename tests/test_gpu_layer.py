@@ -309,7 +309,10 @@ def test_per_rank_subproblems_reproduce_the_full_gemm():
     dict(R=8, S=33, E=32, K=2, B=1, H=192, Hp=320, mode="infer"),  # overflow into home rows
     dict(R=8, S=30, E=928, K=8, B=95, H=64, Hp=64, mode="infer"),  # R*(E+B+1) = 8192, the limit
     dict(R=64, S=8, E=64, K=2, H=64, Hp=128),                  # 64 ranks of one expert, B = 1
-], ids=["E1024", "K1_ragged_tiles", "K32", "R1_B0", "infer_B1", "rows_limit", "R64"])
+    dict(R=8, S=16384, E=64, K=8, H=64, Hp=64),                # over 4096 tile-list entries:
+                                                               # the list built in memory
+], ids=["E1024", "K1_ragged_tiles", "K32", "R1_B0", "infer_B1", "rows_limit", "R64",
+        "tile_list_in_memory"])
 def test_edge_shapes_full_compare(kw):
     """Forward (and backward where the layer trains) compared element by element with
     the oracle at edge shapes of the plan and of the GEMM tiling."""
